@@ -1,0 +1,164 @@
+"""CPU oracle for DDTree tree-verify MLA-absorb attention (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product library never does.  The
+arithmetic lives in ``ddtv_oracle.c`` (plain fp64 C, single-threaded); this file
+only compiles it with gcc, marshals numpy arrays and returns numpy results.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ddtv_oracle.c")
+_LIB = os.path.join(_HERE, "libddtv_oracle.so")
+
+REF_OK, REF_EINVAL, REF_ETREE = 0, 1, 2
+D_LATENT, D_ROPE = 512, 64
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc -O2 (no fast-math).  Returns the library path."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall",
+                               "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def configure(lib):
+    """Declare the C signatures on a loaded oracle library."""
+    P = ctypes.c_void_p
+    i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    lib.ddtvref_build_visibility.argtypes = [P, i32, i32, P, P]
+    lib.ddtvref_verify_attn_rows.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, f64,
+                                             P, i64, P, P, P]
+    lib.ddtvref_row_probs.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, f64, i64, P]
+    lib.ddtvref_partial.argtypes = [P, P, P, P, i32, P, i64, f64, P, P, P]
+    lib.ddtvref_merge.argtypes = [i32, P, P, P, P, P]
+    for name in ("ddtvref_build_visibility", "ddtvref_verify_attn_rows",
+                 "ddtvref_row_probs", "ddtvref_partial", "ddtvref_merge", "ddtvref_words"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        _lib = configure(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _p(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def words(q: int) -> int:
+    return (q + 31) // 32
+
+
+def build_visibility(parent: np.ndarray):
+    """parent int32 [B][Q] -> (bits uint32 [B][Q][W], bad int32 [B], rc)."""
+    parent = _c(parent, np.int32)
+    B, Q = parent.shape
+    bits = np.zeros((B, Q, words(Q)), dtype=np.uint32)
+    bad = np.zeros(B, dtype=np.int32)
+    rc = _load().ddtvref_build_visibility(_p(parent), B, Q, _p(bits), _p(bad))
+    return bits, bad, rc
+
+
+def _kv(a, kv_dtype):
+    return _c(a, np.float32 if kv_dtype == 0 else np.uint16)
+
+
+def verify_attn(q_abs, q_rope, ckv, k_rope, kv_dtype, prefix, bits, scale, rows=None,
+                want_psum=False):
+    """Attention of the given flat query rows (all rows when ``rows`` is None).
+
+    Returns (out float64 [n][512], lse float64 [n]) plus psum [n] when asked.
+    """
+    q_abs = _c(q_abs, np.float32)
+    q_rope = _c(q_rope, np.float32)
+    B, Q, H, _ = q_abs.shape
+    ckv, k_rope = _kv(ckv, kv_dtype), _kv(k_rope, kv_dtype)
+    prefix = _c(prefix, np.int32)
+    bits = _c(bits, np.uint32)
+    if rows is None:
+        n = B * Q * H
+        rows_p = None
+    else:
+        rows = _c(rows, np.int64)
+        n = rows.shape[0]
+        rows_p = rows
+    out = np.zeros((n, D_LATENT), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    psum = np.zeros(n, dtype=np.float64) if want_psum else None
+    rc = _load().ddtvref_verify_attn_rows(_p(q_abs), _p(q_rope), _p(ckv), _p(k_rope), kv_dtype,
+                                          B, Q, H, _p(prefix), _p(bits), float(scale),
+                                          _p(rows_p), n, _p(out), _p(lse), _p(psum))
+    if rc != REF_OK:
+        raise ValueError(f"oracle verify_attn failed with code {rc}")
+    return (out, lse, psum) if want_psum else (out, lse)
+
+
+def row_probs(q_abs, q_rope, ckv, k_rope, kv_dtype, prefix, bits, scale, row):
+    q_abs = _c(q_abs, np.float32)
+    q_rope = _c(q_rope, np.float32)
+    B, Q, H, _ = q_abs.shape
+    prefix = _c(prefix, np.int32)
+    b = row // (Q * H)
+    probs = np.zeros(int(prefix[b]) + Q, dtype=np.float64)
+    rc = _load().ddtvref_row_probs(_p(q_abs), _p(q_rope), _p(_kv(ckv, kv_dtype)),
+                                   _p(_kv(k_rope, kv_dtype)), kv_dtype, B, Q, H, _p(prefix),
+                                   _p(_c(bits, np.uint32)), float(scale), int(row), _p(probs))
+    if rc != REF_OK:
+        raise ValueError(f"oracle row_probs failed with code {rc}")
+    return probs
+
+
+def partial(qa, qr, ckv, k_rope, kv_dtype, idx, scale):
+    """Unnormalised partial (m, l, o[512]) of one query vector over cache rows ``idx``."""
+    qa = _c(qa, np.float32).reshape(D_LATENT)
+    qr = _c(qr, np.float32).reshape(D_ROPE)
+    idx = _c(idx, np.int64).reshape(-1)
+    m = ctypes.c_double()
+    l = ctypes.c_double()
+    o = np.zeros(D_LATENT, dtype=np.float64)
+    rc = _load().ddtvref_partial(_p(qa), _p(qr), _p(_kv(ckv, kv_dtype)), _p(_kv(k_rope, kv_dtype)),
+                                 kv_dtype, _p(idx), idx.shape[0], float(scale),
+                                 ctypes.byref(m), ctypes.byref(l), _p(o))
+    if rc != REF_OK:
+        raise ValueError(f"oracle partial failed with code {rc}")
+    return m.value, l.value, o
+
+
+def merge(m, l, o):
+    """Log-sum-exp merge of S partials -> (out [512], lse)."""
+    m = _c(m, np.float64).reshape(-1)
+    l = _c(l, np.float64).reshape(-1)
+    o = _c(o, np.float64).reshape(-1, D_LATENT)
+    out = np.zeros(D_LATENT, dtype=np.float64)
+    lse = ctypes.c_double()
+    _load().ddtvref_merge(m.shape[0], _p(m), _p(l), _p(o), _p(out), ctypes.byref(lse))
+    return out, lse.value
+
+
+def attend_workload(w, rows=None, bits=None):
+    """Convenience: oracle bits (unless given) + attention for a workloads.Workload."""
+    if bits is None:
+        bits, _, _ = build_visibility(w.parent)
+    return verify_attn(w.q_abs, w.q_rope, w.ckv, w.k_rope, w.kv_dtype, w.prefix, bits,
+                       w.scale, rows=rows)

@@ -1,0 +1,83 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a private copy of the oracle source (string
+substitution on the C text), compiles it with gcc into a temporary directory,
+swaps it in for the real oracle and runs a group of pins from
+test_oracle_pins.py.  At least one pin must fail for every planted mistake.
+Nothing here touches the committed oracle or any GPU code.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ddtv_oracle.c")
+
+# (id, original text, mutated text)
+MUTATIONS = [
+    ("drop_rope_term", "rope += (double)qr[t] *", "rope += 0.0 * (double)qr[t] *"),
+    ("rope_sign", "return scale * (nope + rope);", "return scale * (nope - rope);"),
+    ("no_scale", "return scale * (nope + rope);", "return (nope + rope);"),
+    ("transposed_value_index",
+     "out[d] += s[j] * kv_value(ckv, kv_dtype, row * D_LAT + d);",
+     "out[d] += s[j] * kv_value(ckv, kv_dtype, row * D_LAT + (d ^ 1));"),
+    ("value_from_next_row",
+     "out[d] += s[j] * kv_value(ckv, kv_dtype, row * D_LAT + d);",
+     "out[d] += s[j] * kv_value(ckv, kv_dtype, (row > 0 ? row - 1 : row) * D_LAT + d);"),
+    ("kv_offset_ignores_tree_rows", "off += (int64_t)prefix[i] + Q;", "off += (int64_t)prefix[i];"),
+    ("prefix_off_by_one", "if (j < P) return 1;", "if (j <= P) return 1;"),
+    ("walk_skips_root", "cur = par[cur];\n", "cur = par[cur];\n                if (cur == 0) break;\n"),
+    ("walk_skips_self", "row[cur / 32] |= 1u << (cur % 32);",
+     "if (cur != i) row[cur / 32] |= 1u << (cur % 32);"),
+    ("bits_msb_first", "row[cur / 32] |= 1u << (cur % 32);", "row[cur / 32] |= 1u << (31 - cur % 32);"),
+    ("lse_drops_max", "*lse = m + log(l);", "*lse = log(l);"),
+    ("no_normalise", "for (int d = 0; d < D_LAT; ++d) out[d] /= l;", ""),
+    ("merge_ignores_rescale", "L += w * l[s];", "L += l[s];"),
+    ("head_index_swapped", "int h = (int)(r % H);\n        int q = (int)((r / H) % Q);",
+     "int q = (int)(r % Q);\n        int h = (int)((r / Q) % H);"),
+    ("bf16_misread", "uint32_t u = ((uint32_t)h) << 16;", "uint32_t u = ((uint32_t)h) << 15;"),
+    ("accept_root_with_parent", "if (i == 0) return par[0] == -1;", "if (i == 0) return 1;"),
+]
+
+PINS = [
+    pins.test_closed_form_latent_scores,
+    pins.test_closed_form_rope_scores_value_excludes_rope,
+    pins.test_bf16_widening_exact,
+    lambda: pins.test_chain_equals_causal(0),
+    lambda: pins.test_chain_equals_causal(1),
+    pins.test_single_query_equals_dense,
+    pins.test_single_bit_mask_exact,
+    lambda: pins.test_small_configs_match_torch("c2"),
+    lambda: pins.test_bruteforce_masks(5),
+    lambda: pins.test_lse_merge_identity(0),
+    pins.test_invalid_trees_reported,
+    pins.test_scale_zero_is_mean,
+]
+
+
+@pytest.mark.parametrize("mid,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_mutation(tmp_path, mid, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor for {mid} not found"
+    mutated = src.replace(old, new, 1)
+    c = tmp_path / "mut.c"
+    so = tmp_path / "libmut.so"
+    c.write_text(mutated)
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", str(so), str(c), "-lm"])
+    lib = oracle.configure(ctypes.CDLL(str(so)))
+    saved = oracle._lib
+    oracle._lib = lib
+    failed = []
+    try:
+        for pin in PINS:
+            try:
+                pin()
+            except (AssertionError, ValueError):
+                failed.append(getattr(pin, "__name__", "lambda"))
+    finally:
+        oracle._lib = saved
+    assert failed, f"no pin caught mutation {mid}"

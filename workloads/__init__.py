@@ -1,0 +1,248 @@
+"""Seeded synthetic inputs for tree-verify MLA-absorb attention.
+
+This module only draws inputs: tree shapes, prefix lengths and the query / latent
+KV tensors. It holds none of the attention arithmetic and none of the visibility
+logic, so both the CPU oracle and the HIP path can consume what it produces
+without sharing any of the computation.
+
+Shapes follow the pages' description of the verify step (absorbed 512-d query
+plus a 64-d rope query per (token, head); one 512-d latent plus one 64-d rope key
+per cached position, shared by all heads) -- "The Verify-Attn Kernel: A Single
+File Write ...", section "The Design Journey: From Concept to CUDA", and the
+latent/rope sizes in its section "Assumptions and the Path Forward".
+
+Recipe (for every workload):
+  * numpy PCG64 ``default_rng(seed)``;
+  * draw order: trees, prefixes, q_abs, q_rope, ckv, k_rope;
+  * float32 tensors are ``standard_normal(dtype=float32) * sigma``;
+  * bf16 tensors are the float32 draw rounded to nearest-even on the bit pattern.
+"""
+from __future__ import annotations
+
+import heapq
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+D_LATENT = 512
+D_ROPE = 64
+SCALE_192 = 1.0 / math.sqrt(192.0)
+
+F32 = 0
+BF16 = 1
+
+
+# --------------------------------------------------------------------------- trees
+def uniform_tree(rng: np.random.Generator, q: int) -> np.ndarray:
+    """Random recursive tree: parent[0] = -1, parent[i] uniform in [0, i)."""
+    p = np.empty(q, dtype=np.int32)
+    p[0] = -1
+    for i in range(1, q):
+        p[i] = rng.integers(0, i)
+    return p
+
+
+def chain_tree(q: int) -> np.ndarray:
+    """Linear chain: parent[i] = i - 1 (the prefill / causal shape)."""
+    p = np.arange(-1, q - 1, dtype=np.int32)
+    return p
+
+
+def best_first_tree(rng: np.random.Generator, q: int, depth_cap: int,
+                    vocab: int = 32, topk: int = 4, logit_sigma: float = 2.0) -> np.ndarray:
+    """Tree shaped like a best-first draft expansion.
+
+    The root has score 0.  Whenever a node at depth < depth_cap is added, ``vocab``
+    logits ~ N(0, logit_sigma^2) are drawn, and the ``topk`` best log-softmax
+    entries become candidate children with score parent_score + log p.  Candidates
+    are popped from a max-heap (ties by push order) until ``q`` nodes exist, so
+    parents always precede children, every internal node has 1..topk children and
+    the depth (in edges, root = 0) never exceeds ``depth_cap``.
+    """
+    parent = np.empty(q, dtype=np.int32)
+    parent[0] = -1
+    depth = [0]
+    score = [0.0]
+    heap: list[tuple[float, int, int]] = []
+    pushes = 0
+
+    def expand(node: int) -> None:
+        nonlocal pushes
+        if depth[node] >= depth_cap:
+            return
+        logits = rng.standard_normal(vocab) * logit_sigma
+        mx = logits.max()
+        logp = logits - (mx + math.log(np.exp(logits - mx).sum()))
+        top = np.argsort(-logp, kind="stable")[:topk]
+        for t in top:
+            heapq.heappush(heap, (-(score[node] + float(logp[t])), pushes, node))
+            pushes += 1
+
+    expand(0)
+    n = 1
+    while n < q:
+        if not heap:
+            raise RuntimeError("best-first expansion ran out of candidates")
+        neg, _, par = heapq.heappop(heap)
+        parent[n] = par
+        depth.append(depth[par] + 1)
+        score.append(-neg)
+        expand(n)
+        n += 1
+    return parent
+
+
+def tree_depths(parent: np.ndarray) -> np.ndarray:
+    """Depth in edges of each node of a topologically ordered tree (input helper)."""
+    d = np.zeros(len(parent), dtype=np.int32)
+    for i in range(1, len(parent)):
+        d[i] = d[parent[i]] + 1
+    return d
+
+
+# --------------------------------------------------------------------------- tensors
+def round_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> 16) & 1
+    r = (u.astype(np.uint64) + 0x7FFF + lsb) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (h.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class Workload:
+    name: str
+    B: int
+    H: int
+    Q: int
+    prefix: np.ndarray            # int32 [B]
+    parent: np.ndarray            # int32 [B][Q]
+    q_abs: np.ndarray             # float32 [B][Q][H][512]
+    q_rope: np.ndarray            # float32 [B][Q][H][64]
+    ckv: np.ndarray               # float32 or uint16(bf16 bits) [sum KV][512]
+    k_rope: np.ndarray            # same dtype [sum KV][64]
+    kv_dtype: int                 # F32 or BF16
+    scale: float
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def kv_len(self) -> np.ndarray:
+        return self.prefix.astype(np.int64) + self.Q
+
+    @property
+    def kv_off(self) -> np.ndarray:
+        """Row offset of each batch row in the packed cache (rows back to back)."""
+        off = np.zeros(self.B + 1, dtype=np.int64)
+        off[1:] = np.cumsum(self.kv_len)
+        return off
+
+    @property
+    def total_kv(self) -> int:
+        return int(self.kv_len.sum())
+
+    def with_parent(self, parent: np.ndarray, name: str | None = None) -> "Workload":
+        w = Workload(**{**self.__dict__})
+        w.parent = np.ascontiguousarray(parent, dtype=np.int32).reshape(self.B, self.Q)
+        w.name = name or self.name
+        return w
+
+
+def make_workload(name: str, seed: int, B: int, H: int, Q: int, prefix,
+                  tree: str = "uniform", depth_cap: int = 0,
+                  q_sigma: float = 1.0, kv_sigma: float = 1.0,
+                  kv_dtype: int = F32, scale: float = SCALE_192) -> Workload:
+    """Draw one workload.  ``prefix`` is an int, a sequence of B ints, or a
+    (lo, hi) range given as ``("uniform", lo, hi)`` (inclusive)."""
+    rng = np.random.default_rng(seed)
+    # 1. trees
+    if tree == "uniform":
+        parent = np.stack([uniform_tree(rng, Q) for _ in range(B)])
+    elif tree == "chain":
+        parent = np.stack([chain_tree(Q) for _ in range(B)])
+    elif tree == "best_first":
+        parent = np.stack([best_first_tree(rng, Q, depth_cap) for _ in range(B)])
+    else:
+        raise ValueError(tree)
+    # 2. prefixes
+    if isinstance(prefix, tuple) and prefix and prefix[0] == "uniform":
+        pre = rng.integers(prefix[1], prefix[2] + 1, size=B).astype(np.int32)
+    elif np.isscalar(prefix):
+        pre = np.full(B, int(prefix), dtype=np.int32)
+    else:
+        pre = np.asarray(prefix, dtype=np.int32).reshape(B)
+    total_kv = int((pre.astype(np.int64) + Q).sum())
+    # 3. tensors
+    q_abs = rng.standard_normal((B, Q, H, D_LATENT), dtype=np.float32)
+    if q_sigma != 1.0:
+        q_abs *= np.float32(q_sigma)
+    q_rope = rng.standard_normal((B, Q, H, D_ROPE), dtype=np.float32)
+    if q_sigma != 1.0:
+        q_rope *= np.float32(q_sigma)
+    ckv = rng.standard_normal((total_kv, D_LATENT), dtype=np.float32)
+    if kv_sigma != 1.0:
+        ckv *= np.float32(kv_sigma)
+    k_rope = rng.standard_normal((total_kv, D_ROPE), dtype=np.float32)
+    if kv_sigma != 1.0:
+        k_rope *= np.float32(kv_sigma)
+    if kv_dtype == BF16:
+        ckv = round_bf16_bits(ckv)
+        k_rope = round_bf16_bits(k_rope)
+    return Workload(name=name, B=B, H=H, Q=Q, prefix=pre, parent=parent.astype(np.int32),
+                    q_abs=q_abs, q_rope=q_rope, ckv=ckv, k_rope=k_rope,
+                    kv_dtype=kv_dtype, scale=float(scale),
+                    meta=dict(seed=seed, tree=tree, depth_cap=depth_cap,
+                              q_sigma=q_sigma, kv_sigma=kv_sigma))
+
+
+# --------------------------------------------------------------------------- the five workloads
+# c1..c5: the five verify-attention workloads (sizes as named).  Seeds are 1000 + index.
+CONFIGS = {
+    "c1": dict(B=1, H=8, Q=9, prefix=0, tree="uniform"),
+    "c2": dict(B=3, H=8, Q=9, prefix=37, tree="uniform"),
+    "c3": dict(B=1, H=16, Q=64, prefix=4096, tree="best_first", depth_cap=8, kv_sigma=0.5),
+    "c4": dict(B=8, H=16, Q=128, prefix=32768, tree="best_first", depth_cap=12),
+    "c5": dict(B=32, H=64, Q=64, prefix=("uniform", 1024, 131072), tree="uniform", kv_dtype=BF16),
+}
+
+DESCRIPTIONS = {
+    "c1": "B=1 H=8 prefix=0 q_len=9 uniform tree fp32",
+    "c2": "B=3 H=8 prefix=37 q_len=9 uniform trees fp32",
+    "c3": "B=1 H=16 prefix=4096 q_len=64 best-first tree (depth<=8) fp32, KV sigma 0.5",
+    "c4": "B=8 H=16 prefix=32768 q_len=128 best-first trees (depth<=12) fp32",
+    "c5": "B=32 H=64 prefix~U[1024,131072] q_len=64 uniform trees bf16 KV",
+}
+
+
+def config(name: str, seed: int | None = None, **override) -> Workload:
+    idx = int(name[1:])
+    kw = dict(CONFIGS[name])
+    kw.update(override)
+    return make_workload(name, 1000 + idx if seed is None else seed, **kw)
+
+
+def c2_chain() -> Workload:
+    """c2's tensors with every tree replaced by a chain (must equal causal attention)."""
+    w = config("c2")
+    return w.with_parent(np.stack([chain_tree(w.Q) for _ in range(w.B)]), name="c2-chain")
+
+
+def sample_rows(w: Workload, n: int, seed: int = 7) -> np.ndarray:
+    """Seeded sample of n flat query-row ids (b*Q + q)*H + h spread over all batch rows."""
+    rng = np.random.default_rng(seed)
+    total = w.B * w.Q * w.H
+    if n >= total:
+        return np.arange(total, dtype=np.int64)
+    per_b = [n // w.B + (1 if b < n % w.B else 0) for b in range(w.B)]
+    rows = []
+    for b, k in enumerate(per_b):
+        if k == 0:
+            continue
+        local = rng.choice(w.Q * w.H, size=k, replace=False)
+        rows.append(b * w.Q * w.H + np.sort(local))
+    return np.concatenate(rows).astype(np.int64)
