@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark: DDTree tree-verify MLA-absorb attention on one MI355X.
+
+One step = one verify pass of the whole hot path over one batch: the visibility
+build (parent arrays -> packed ancestor masks), the masked absorbed-MLA attention
+and, when the cache is split, the log-sum-exp merge.  Inputs are seeded and
+synthetic and already resident in HBM when the timed region starts.
+
+Prints ONE JSON line.  The default workload is B=8, H=16, prefix 32768,
+q_len 128, best-first trees, fp32 cache (``--config c4``).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tree-verify attn: achieved HBM GB/s (% of peak) and tree-query tokens/sec"
+HBM_PEAK_GBPS = 8000.0
+PEAK_TFLOPS = {"f32-mfma": 157.3, "bf16-mfma": 2500.0}
+KERNEL_SOURCES = ["attn_mfma.hip", "attn_valu.hip", "merge.hip", "visibility.hip", "api.hip",
+                  "ddtv_internal.hpp"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- HIP events (ctypes)
+class Hip:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, stream) == 0
+
+    def elapsed_ms(self, a, b):
+        self.lib.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+
+# ----------------------------------------------------------------------------- algorithmic counts
+def algorithmic(w):
+    """Bytes every step must move at least once and flops of the visible pairs.
+
+    bytes: q_abs + q_rope + each cache row once (latent + rope) + out + lse + parents +
+           masks + prefix lengths.
+    flops: 2 * (512 + 64) for the score plus 2 * 512 for the weighted sum, per visible
+           (query row, cache position) pair.
+    """
+    import workloads as wl
+    esz = 2 if w.kv_dtype == wl.BF16 else 4
+    rows = w.B * w.Q * w.H
+    W = (w.Q + 31) // 32
+    nbytes = (rows * 576 * 4 + w.total_kv * 576 * esz + rows * 512 * 4 + rows * 4
+              + w.B * w.Q * 4 + w.B * w.Q * W * 4 + w.B * 4)
+    vis_pairs = 0
+    for b in range(w.B):
+        depth = wl.tree_depths(w.parent[b])
+        vis_pairs += w.H * int((int(w.prefix[b]) + depth + 1).sum())
+    flops = vis_pairs * 2 * (576 + 512)
+    return nbytes, flops, vis_pairs
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tree_masked_mla_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(config_name, kernel_hash):
+    """HBM bytes per launch of the attention kernel from committed rocprofv3 PMC
+    summaries (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration),
+    or None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_attn_{config_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_hash:
+        return None
+    return t.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- CPU baseline (oracle)
+def cpu_baseline(w, budget_s=15.0, max_rows=4096):
+    """The oracle (single-threaded fp64 C) on a seeded sample of query rows of the
+    same workload, for about budget_s seconds.  Reported as tree-query tokens/s
+    (rows/s divided by H: one token is one tree node across all heads)."""
+    import oracle
+    import workloads as wl
+    bits, _, _ = oracle.build_visibility(w.parent)
+    rows = wl.sample_rows(w, max_rows, seed=11)
+    done = 0
+    t0 = time.perf_counter()
+    while done < len(rows) and time.perf_counter() - t0 < budget_s:
+        k = min(8, len(rows) - done)
+        oracle.verify_attn(w.q_abs, w.q_rope, w.ckv, w.k_rope, w.kv_dtype, w.prefix, bits, w.scale,
+                           rows=rows[done:done + k])
+        done += k
+    dt = time.perf_counter() - t0
+    return {"value": round(done / dt / w.H, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} seeded (b,q,h) query rows of the same workload (all batch rows), "
+                      f"{dt:.1f} s on 1 host core ({platform.processor() or platform.machine()}); "
+                      f"tokens/s = rows/s / H"}
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
+    ap.add_argument("--split-len", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="instead of the bench, run N launches of a plain copy of the cache bytes "
+                         "(for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as wl
+    import tree_masked_mla_amd as dd
+    from tree_masked_mla_amd.runner import DeviceRun
+
+    dd.load()   # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log(f"generating {args.config}: {wl.DESCRIPTIONS[args.config]}")
+    w = wl.config(args.config)
+
+    if args.copy_calibration:
+        nbytes = w.ckv.nbytes
+        src = torch.from_numpy(np.ascontiguousarray(w.ckv).view(np.uint8)).to(dev).view(torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(args.copy_calibration):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes,
+                          "launches": args.copy_calibration}))
+        return
+
+    r = DeviceRun(w, device=dev, path=args.path, split_len=args.split_len, want_lse=True)
+    rc, path, split_len, n_split, wgs = r.plan()
+    log(f"plan: path={path} split_len={split_len} n_split={n_split} workgroups={wgs}")
+    hip = Hip()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    K = args.steps
+    ev_attn = [(hip.event(), hip.event()) for _ in range(K)]
+    ev_step0, ev_step1 = hip.event(), hip.event()
+
+    for _ in range(args.warmup):
+        r.step(stream)
+    torch.cuda.synchronize()
+
+    t_host0 = time.perf_counter()
+    hip.record(ev_step0, stream)
+    for k in range(K):
+        opts = dd.make_opts(args.path, args.split_len, ev_attn[k][0], ev_attn[k][1])
+        r.step(stream, opts)
+    hip.record(ev_step1, stream)
+    torch.cuda.synchronize()
+    t_host1 = time.perf_counter()
+
+    total_ms = hip.elapsed_ms(ev_step0, ev_step1)
+    attn_ms = [hip.elapsed_ms(a, b) for a, b in ev_attn]
+    ms_step = total_ms / K
+    attn_avg_ms = float(np.mean(attn_ms))
+
+    nbytes, flops, vis_pairs = algorithmic(w)
+    tokens = w.B * w.Q
+    value = tokens / (ms_step / 1e3)
+    hbm_gbps = nbytes / (ms_step / 1e3) / 1e9
+    peak_key = "f32-mfma"       # the cache tile is widened to fp32 and contracted on fp32 MFMA
+    achieved_tflops = flops / (attn_avg_ms / 1e3) / 1e12
+    khash = kernel_source_hash()
+    traffic = load_traffic(args.config, khash)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.kv_dtype == wl.F32 else "bf16-kv/f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {wl.DESCRIPTIONS[args.config]}", "B": w.B, "H": w.H,
+                   "q_len": w.Q, "prefix": "ragged" if args.config == "c5" else int(w.prefix[0]),
+                   "total_kv_rows": w.total_kv, "scale": w.scale, "path": path, "split_len": split_len,
+                   "n_split": n_split, "workgroups": wgs},
+        "hbm_gbps": round(hbm_gbps, 2),
+        "hbm_pct_of_peak": round(100.0 * hbm_gbps / HBM_PEAK_GBPS, 3),
+        "attn_kernel_us": round(attn_avg_ms * 1e3, 2),
+        "step_us": round(ms_step * 1e3, 2),
+        "host_wall_ms_per_step": round((t_host1 - t_host0) * 1e3 / K, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved_tflops, 3),
+            "peak": PEAK_TFLOPS[peak_key],
+            "unit": "TFLOP/s",
+            "frac": round(achieved_tflops / PEAK_TFLOPS[peak_key], 4),
+            "traffic": traffic,
+            "kernel": "attn_mfma_kernel" if path == 2 else "attn_valu_kernel",
+            "flops_per_launch": flops,
+            "algorithmic_bytes_per_step": nbytes,
+            "visible_pairs": vis_pairs,
+            "kernel_source_hash": khash,
+        },
+    }
+    if not args.no_cpu:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(w, budget_s=args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+/*
+ * ddtv.h -- DDTree tree-verify MLA-absorb attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  A draft tree of Q nodes (the root counts as a node) is verified
+ * against one batch row of a multi-head latent attention (MLA) KV cache.  For
+ * every (batch row b, tree node q, head h) the score against cache position j is
+ *
+ *     s_j = scale * ( q_abs[b,q,h,:] . ckv[j,:]  +  q_rope[b,q,h,:] . k_rope[j,:] )
+ *
+ * (512-d absorbed query against the 512-d cached latent, plus the 64-d rope
+ * query against the 64-d rope key), a softmax runs over the positions the node
+ * may see -- the whole shared prefix, its tree ancestors and itself -- and the
+ * output is the softmax-weighted sum of the 512-d latents.  The per-head value
+ * projection is NOT applied here; the caller runs it as a separate GEMM.
+ *   Pages: "The Verify-Attn Kernel: A Single File Write That Completed a Critical
+ *   Piece of the DDTree Engine", sections "The Design Journey: From Concept to
+ *   CUDA" and "Design Decisions and Trade-Offs"; "The Moment of Truth:
+ *   Validating a Custom CUDA Attention Kernel for Speculative Decoding",
+ *   section "The Design Journey: From Theory to Silicon".
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers unless marked HOST.  The caller allocates and
+ *     owns every buffer; the library never allocates, frees or synchronises,
+ *     except ddtv_read_status (which synchronises the stream on purpose).
+ *   - All device work is enqueued on `stream` and is asynchronous.
+ *   - Argument checks happen on the host before any HIP call and return an error
+ *     without touching the device.  Device-side launch failures map to
+ *     DDTV_EDEVICE.  No exception crosses this interface.
+ *   - Device pointers to float data must be 16-byte aligned.
+ *   - Calls are stateless and re-entrant; calls on different streams may overlap.
+ */
+#ifndef DDTV_H
+#define DDTV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DDTV_D_LATENT 512 /* latent (absorbed) width */
+#define DDTV_D_ROPE 64    /* rope width */
+#define DDTV_MAX_Q 256    /* largest supported tree (nodes incl. root) */
+
+typedef enum {
+    DDTV_OK = 0,
+    DDTV_EINVAL = 1,       /* bad argument (null/misaligned pointer, bad size or scale) */
+    DDTV_ETREE = 2,        /* a parent array is not a topologically ordered tree */
+    DDTV_EUNSUPPORTED = 3, /* unsupported dtype, path or shape */
+    DDTV_EWORKSPACE = 4,   /* workspace (or visibility buffer) too small */
+    DDTV_EDEVICE = 5       /* a HIP call or kernel launch failed */
+} ddtv_status;
+
+typedef enum { DDTV_F32 = 0, DDTV_BF16 = 1 } ddtv_dtype;
+
+/* Per batch-row cache geometry, kept on the device (16 bytes). */
+typedef struct {
+    int64_t kv_off; /* first cache row of batch row b */
+    int32_t prefix; /* P_b, shared-prefix length */
+    int32_t kv_len; /* P_b + Q */
+} ddtv_row;
+
+/*
+ * Visibility of a batch of trees (HOST struct, caller-owned; filled by
+ * ddtv_build_visibility; plain data, so callers may also fill `bits` themselves).
+ *
+ * Tree node a of batch row b sits at cache row rows[b].kv_off + rows[b].prefix + a
+ * (new KV rows are written right after the prefix, in node order -- "The
+ * Architecture of an Inference Engine: Designing the Model Structure for DDTree
+ * Speculative Decoding", section "What the Message Actually Says").  Batch rows
+ * are packed back to back: kv_off(b) = sum over b' < b of (P_b' + Q).
+ *
+ * bits: word w, bit k (LSB first) of node i is set iff node 32w+k is i or an
+ * ancestor of i.  Bits at positions >= Q are zero.  The prefix is implicit
+ * (always visible) and has no bits.
+ */
+typedef struct {
+    int32_t B, Q, W;     /* batch rows, tree nodes, mask words per node = ceil(Q/32) */
+    int32_t max_kv;      /* max_b (P_b + Q) */
+    int64_t total_kv;    /* sum_b (P_b + Q): cache rows spanned by the batch */
+    uint32_t *bits;      /* DEVICE [B][Q][W] */
+    ddtv_row *rows;      /* DEVICE [B] */
+    int32_t *status;     /* DEVICE [B]: -1 if row b is a valid tree, else its lowest bad node */
+    const int32_t *prefix_host; /* HOST [B] or NULL: BORROWED from the build call; when set it
+                                   must stay valid until the last verify call that plans with
+                                   this struct returns (used only to balance KV splits) */
+} ddtv_vis;
+
+/* Bytes of device memory ddtv_build_visibility needs for B trees of Q nodes
+ * (0 if B < 1 or Q outside 1..DDTV_MAX_Q). */
+size_t ddtv_vis_bytes(int32_t B, int32_t Q);
+
+/*
+ * S1: turn parent arrays into packed ancestor-or-self bit masks.
+ *   Pages: "The Verify-Attn Kernel ...", section "The Design Journey" (each node
+ *   sees the shared prefix and its tree ancestors); "The Architecture of an
+ *   Inference Engine ...", section "Assumptions Embedded in the Design" (mask
+ *   format left open; it is fixed here as packed bits).
+ *
+ *   parent     DEVICE int32 [B][Q].  parent[b][0] must be -1 (the root) and
+ *              0 <= parent[b][i] < i for i >= 1 (parents precede children).
+ *   prefix_len HOST int32 [B], each >= 0 (the host-tracked cache end).  Read
+ *              during the call; its address is also stored in vis->prefix_host,
+ *              so keep it alive while the struct is used for verify calls (or set
+ *              vis->prefix_host to NULL afterwards).
+ *   vis_buf    DEVICE buffer of at least ddtv_vis_bytes(B, Q) bytes, 256-byte
+ *              aligned; bits, rows and status are carved out of it.
+ *   vis        HOST struct filled on return (pointers into vis_buf).
+ * Malformed trees are detected ON THE DEVICE: the call still returns DDTV_OK and
+ * the lowest malformed node of each row is written to vis->status; a malformed
+ * node sees only itself, and the ancestor chain of any node stops at the first
+ * malformed node it meets (that node included), so attention stays defined.
+ * Use ddtv_read_status to turn that into DDTV_ETREE.
+ * Host-detected errors: DDTV_EINVAL (null pointers, B < 1, Q outside 1..256,
+ * negative prefix, sum of KV rows >= 2^31 per row), DDTV_EWORKSPACE (vis_buf too
+ * small).
+ */
+ddtv_status ddtv_build_visibility(const int32_t *parent, const int32_t *prefix_len,
+                                  int32_t B, int32_t Q, void *vis_buf, size_t vis_buf_bytes,
+                                  ddtv_vis *vis, hipStream_t stream);
+
+/*
+ * Synchronise `stream`, read vis->status and report the first malformed tree.
+ *   bad_row, bad_node  HOST out (may be NULL): the lowest batch row with a
+ *                      malformed tree and its lowest malformed node, or -1/-1.
+ * Returns DDTV_OK, DDTV_ETREE, DDTV_EINVAL or DDTV_EDEVICE.  Not for hot loops.
+ */
+ddtv_status ddtv_read_status(const ddtv_vis *vis, int32_t *bad_row, int32_t *bad_node,
+                             hipStream_t stream);
+
+/* Execution path of the attention step. */
+typedef enum {
+    DDTV_PATH_AUTO = 0, /* VALU when Q < 16, MFMA otherwise */
+    DDTV_PATH_VALU = 1, /* vector-ALU kernel (any Q) */
+    DDTV_PATH_MFMA = 2  /* matrix-core kernel (any Q) */
+} ddtv_path;
+
+/* Optional controls for ddtv_verify_attn_ex (zero-initialise for defaults). */
+typedef struct {
+    int32_t path;          /* ddtv_path */
+    int32_t split_len;     /* KV positions per split; 0 = automatic; else a multiple of 64 */
+    hipEvent_t attn_begin; /* if non-NULL: recorded on `stream` right before the main kernel */
+    hipEvent_t attn_end;   /* if non-NULL: recorded on `stream` right after it (before the merge) */
+} ddtv_opts;
+
+/* Workspace bytes ddtv_verify_attn(_ex) needs for this visibility, head count and
+ * KV dtype (0 when no KV split is planned).  opts may be NULL. */
+size_t ddtv_workspace_bytes(const ddtv_vis *vis, int32_t H, ddtv_dtype kv_dtype);
+size_t ddtv_workspace_bytes_ex(const ddtv_vis *vis, int32_t H, ddtv_dtype kv_dtype,
+                               const ddtv_opts *opts);
+
+/*
+ * S2..S7: masked absorbed-MLA attention of every (b, q, h) query row.
+ *   Pages: "The Verify-Attn Kernel ...", sections "The Design Journey: From
+ *   Concept to CUDA" (scores, max-subtracted softmax over visible positions,
+ *   weighted latent sum), "Design Decisions and Trade-Offs" (latent output,
+ *   separate value GEMM; long prefixes split and merged through log-sum-exp).
+ *
+ *   q_abs   DEVICE float [B][Q][H][512]  absorbed (nope) query, token-major
+ *   q_rope  DEVICE float [B][Q][H][64]   rotated rope query
+ *   ckv     DEVICE [vis->total_kv][512]  latent cache, float or bf16 per kv_dtype
+ *   k_rope  DEVICE [vis->total_kv][64]   rotated rope keys, same dtype
+ *   H       heads (>= 1); every head shares the one latent cache
+ *   vis     HOST struct from ddtv_build_visibility (bits/rows must be complete on
+ *           `stream` by the time the kernels run)
+ *   scale   softmax scale applied to the summed dot product (finite)
+ *   out     DEVICE float [B][Q][H][512]  softmax-weighted latent sum
+ *   lse     DEVICE float [B][Q][H] or NULL: natural-log log-sum-exp of the scaled
+ *           scores (-inf for a row that sees nothing)
+ *   workspace, workspace_bytes  DEVICE scratch of at least ddtv_workspace_bytes()
+ *           (may be NULL when that is 0), 256-byte aligned
+ * A row that sees no position (possible only with a hand-made mask) gets out = 0
+ * and lse = -inf.  Errors: DDTV_EINVAL, DDTV_EUNSUPPORTED, DDTV_EWORKSPACE,
+ * DDTV_EDEVICE.
+ */
+ddtv_status ddtv_verify_attn(const float *q_abs, const float *q_rope, const void *ckv,
+                             const void *k_rope, ddtv_dtype kv_dtype, int32_t H,
+                             const ddtv_vis *vis, float scale, float *out, float *lse,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Same as ddtv_verify_attn with explicit controls (path, split length, timing
+ * events).  opts may be NULL. */
+ddtv_status ddtv_verify_attn_ex(const float *q_abs, const float *q_rope, const void *ckv,
+                                const void *k_rope, ddtv_dtype kv_dtype, int32_t H,
+                                const ddtv_vis *vis, float scale, float *out, float *lse,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                const ddtv_opts *opts);
+
+/* Describes the plan ddtv_verify_attn_ex would run (HOST out params, may be NULL):
+ * path taken, KV positions per split, maximum splits per batch row, workgroups
+ * of the main kernel.  Returns DDTV_EINVAL/DDTV_EUNSUPPORTED like the call would. */
+ddtv_status ddtv_plan_info(const ddtv_vis *vis, int32_t H, ddtv_dtype kv_dtype,
+                           const ddtv_opts *opts, int32_t *path, int32_t *split_len,
+                           int32_t *n_split, int64_t *workgroups);
+
+/* Static description of a status code. */
+const char *ddtv_status_string(ddtv_status s);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int32_t ddtv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDTV_H */

@@ -1,0 +1,186 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import tree_masked_mla_amd as dd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ddtv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dd.LIB_PATH):
+        from tree_masked_mla_amd import build
+        build.build()
+    return dd.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ddtv_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    raw = ctypes.CDLL(dd.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(names) == set(dd.EXPORTED)
+
+
+def test_version_and_strings(lib):
+    assert dd.ddtv_version() == 100
+    for code in range(6):
+        assert dd.ddtv_status_string(code)
+    assert dd.ddtv_status_string(2).startswith("malformed tree")
+
+
+def test_vis_bytes(lib):
+    assert dd.ddtv_vis_bytes(0, 9) == 0
+    assert dd.ddtv_vis_bytes(1, 0) == 0
+    assert dd.ddtv_vis_bytes(1, 257) == 0
+    assert dd.ddtv_vis_bytes(1, 256) > 0
+    for B, Q in [(1, 9), (3, 9), (8, 128), (32, 64), (5, 33)]:
+        W = (Q + 31) // 32
+        need = B * Q * W * 4 + B * 16 + B * 4
+        got = dd.ddtv_vis_bytes(B, Q)
+        assert got >= need and got % 256 == 0
+
+
+FAKE = 1 << 40          # an aligned address that is never dereferenced (checks fail first)
+
+
+def build_call(lib, parent=FAKE, prefix=None, B=2, Q=9, buf=FAKE, nbytes=1 << 20):
+    prefix = np.zeros(max(B, 1), np.int32) if prefix is None else prefix
+    vis = dd.ddtv_vis()
+    return lib.ddtv_build_visibility(parent, prefix.ctypes.data if prefix is not False else None, B, Q, buf,
+                                     nbytes, ctypes.byref(vis), None)
+
+
+def test_build_visibility_host_errors(lib):
+    E = dd.DDTV_EINVAL
+    assert build_call(lib, parent=None) == E
+    assert build_call(lib, prefix=False) == E
+    assert build_call(lib, buf=None) == E
+    assert build_call(lib, B=0) == E
+    assert build_call(lib, Q=0) == E
+    assert build_call(lib, Q=257) == E
+    assert build_call(lib, parent=FAKE + 2) == E                     # misaligned parent
+    assert build_call(lib, buf=FAKE + 16) == E                       # vis_buf not 256-aligned
+    assert build_call(lib, prefix=np.array([3, -1], np.int32)) == E  # negative prefix
+    assert build_call(lib, prefix=np.array([2**31 - 5, 0], np.int32)) == E  # P + Q overflows int32
+    assert build_call(lib, nbytes=dd.ddtv_vis_bytes(2, 9) - 1) == dd.DDTV_EWORKSPACE
+    vis = dd.ddtv_vis()
+    assert lib.ddtv_build_visibility(FAKE, np.zeros(2, np.int32).ctypes.data, 2, 9, FAKE, 1 << 20, None,
+                                     None) == E
+
+
+def fake_vis(B=2, Q=9, prefix=(37, 37)):
+    v = dd.ddtv_vis()
+    v.B, v.Q, v.W = B, Q, (Q + 31) // 32
+    pre = np.asarray(prefix, np.int32)
+    v.max_kv = int(pre.max()) + Q
+    v.total_kv = int((pre.astype(np.int64) + Q).sum())
+    v.bits, v.rows, v.status = FAKE, FAKE + 4096, FAKE + 8192
+    v.prefix_host = pre.ctypes.data
+    return dd.Visibility(v, (pre,))
+
+
+def verify_call(lib, vis, q_abs=FAKE, q_rope=FAKE, ckv=FAKE, k_rope=FAKE, kv_dtype=0, H=8, scale=0.07,
+                out=FAKE, lse=None, ws=None, ws_bytes=0, opts=None):
+    return lib.ddtv_verify_attn_ex(q_abs, q_rope, ckv, k_rope, kv_dtype, H, ctypes.byref(vis.vis),
+                                   ctypes.c_float(scale), out, lse, ws, ws_bytes, None,
+                                   ctypes.byref(opts) if opts is not None else None)
+
+
+def test_verify_host_errors(lib):
+    vis = fake_vis()
+    E, U = dd.DDTV_EINVAL, dd.DDTV_EUNSUPPORTED
+    for kw in ("q_abs", "q_rope", "ckv", "k_rope", "out"):
+        assert verify_call(lib, vis, **{kw: None}) == E, kw
+        assert verify_call(lib, vis, **{kw: FAKE + 4}) == E, kw        # not 16-byte aligned
+    assert verify_call(lib, vis, lse=FAKE + 2) == E
+    assert verify_call(lib, vis, H=0) == E
+    assert verify_call(lib, vis, scale=float("nan")) == E
+    assert verify_call(lib, vis, scale=float("inf")) == E
+    assert verify_call(lib, vis, kv_dtype=2) == U
+    assert verify_call(lib, vis, opts=dd.make_opts(path=3)) == U
+    assert verify_call(lib, vis, opts=dd.make_opts(split_len=100)) == E   # not a multiple of 64
+    assert verify_call(lib, vis, opts=dd.make_opts(split_len=-64)) == E
+    bad = fake_vis()
+    bad.vis.W = 2
+    assert verify_call(lib, bad) == E
+    bad = fake_vis()
+    bad.vis.bits = None
+    assert verify_call(lib, bad) == E
+    bad = fake_vis(Q=9)
+    bad.vis.Q = 300
+    assert verify_call(lib, bad) == E
+    # splitting needs a workspace
+    vis = fake_vis(B=1, Q=64, prefix=(4096,))
+    opts = dd.make_opts(split_len=1024)
+    need = dd.ddtv_workspace_bytes(vis, 16, 0, opts)
+    assert need > 0
+    assert verify_call(lib, vis, H=16, opts=opts) == dd.DDTV_EWORKSPACE
+    assert verify_call(lib, vis, H=16, opts=opts, ws=FAKE, ws_bytes=need - 1) == dd.DDTV_EWORKSPACE
+    assert verify_call(lib, vis, H=16, opts=opts, ws=FAKE + 16, ws_bytes=need) == E
+
+
+def test_plan_rules(lib):
+    # q_len < 16 -> VALU, else MFMA; forced paths honoured
+    for Q, want in [(1, dd.DDTV_PATH_VALU), (9, dd.DDTV_PATH_VALU), (15, dd.DDTV_PATH_VALU),
+                    (16, dd.DDTV_PATH_MFMA), (128, dd.DDTV_PATH_MFMA)]:
+        vis = fake_vis(B=1, Q=Q, prefix=(100,))
+        rc, path, L, ns, wg = dd.ddtv_plan_info(vis, 8, 0)
+        assert rc == 0 and path == want
+    vis = fake_vis(B=1, Q=9, prefix=(100,))
+    assert dd.ddtv_plan_info(vis, 8, 0, dd.make_opts(path=dd.DDTV_PATH_MFMA))[1] == dd.DDTV_PATH_MFMA
+    # a forced split length gives ceil(max_kv / L) splits and a matching workspace
+    vis = fake_vis(B=2, Q=64, prefix=(1000, 5000))
+    opts = dd.make_opts(split_len=1024)
+    rc, path, L, ns, wg = dd.ddtv_plan_info(vis, 16, 0, opts)
+    assert (L, ns) == (1024, (5064 + 1023) // 1024)
+    R = 64 * 16
+    assert wg == 2 * ns * ((R + 63) // 64)
+    ws = dd.ddtv_workspace_bytes(vis, 16, 0, opts)
+    assert ws >= 2 * ns * R * (512 * 4 + 8)
+    # single split: no workspace
+    opts = dd.make_opts(split_len=8192)
+    assert dd.ddtv_workspace_bytes(vis, 16, 0, opts) == 0
+    assert dd.ddtv_plan_info(vis, 16, 0, opts)[3] == 1
+
+
+def test_auto_plan_shapes(lib):
+    """The automatic planner fills the device with small grids and keeps big ones whole."""
+    vis = fake_vis(B=1, Q=64, prefix=(4096,))          # 16 row tiles: must split
+    rc, path, L, ns, wg = dd.ddtv_plan_info(vis, 16, 0)
+    assert rc == 0 and ns > 1 and wg >= 128
+    vis = fake_vis(B=8, Q=128, prefix=(32768,) * 8)    # 256 row tiles of equal work
+    rc, path, L, ns, wg = dd.ddtv_plan_info(vis, 16, 0)
+    assert rc == 0 and wg >= 256
+    assert L % 64 == 0
+
+
+def test_oracle_shares_error_contract(lib):
+    """The oracle rejects the same shapes the library rejects."""
+    o = oracle._load()
+    bits = np.zeros(4, np.uint32)
+    out = np.zeros(512)
+    lse = np.zeros(1)
+    pre = np.array([-1], np.int32)
+    q = np.zeros((1, 1, 1, 512), np.float32)
+    rc = o.ddtvref_verify_attn_rows(q.ctypes.data, q.ctypes.data, q.ctypes.data, q.ctypes.data, 0, 1, 1, 1,
+                                    pre.ctypes.data, bits.ctypes.data, 1.0, None, 0, out.ctypes.data,
+                                    lse.ctypes.data, None)
+    assert rc == oracle.REF_EINVAL == dd.DDTV_EINVAL
+    b, _, rc = oracle.build_visibility(np.array([[0, 0]], np.int32))
+    assert rc == oracle.REF_ETREE == dd.DDTV_ETREE

@@ -1,0 +1,318 @@
+// C ABI of libddtv: host-side argument checks, split planning and launches.
+// Every check runs before the first HIP call, so argument errors are reported
+// identically with or without a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <functional>
+#include <queue>
+#include <vector>
+
+#include "ddtv_internal.hpp"
+
+using namespace ddtv;
+
+namespace {
+
+constexpr int32_t kVersion = 100;   // 0.1.0
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct VisLayout {
+    size_t bits, rows, status, total;
+};
+
+VisLayout vis_layout(int32_t B, int32_t Q) {
+    VisLayout L{};
+    const int W = (Q + 31) / 32;
+    L.bits = 0;
+    L.rows = round_up((size_t)B * Q * W * sizeof(uint32_t), 256);
+    L.status = L.rows + round_up((size_t)B * sizeof(ddtv_row), 256);
+    L.total = L.status + round_up((size_t)B * sizeof(int32_t), 256);
+    return L;
+}
+
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+ddtv_status check_vis(const ddtv_vis* vis) {
+    if (!vis || !vis->bits || !vis->rows) return DDTV_EINVAL;
+    if (vis->B < 1 || vis->Q < 1 || vis->Q > kMaxQ || vis->W != (vis->Q + 31) / 32) return DDTV_EINVAL;
+    if (vis->max_kv < vis->Q || vis->total_kv < (int64_t)vis->B * vis->Q) return DDTV_EINVAL;
+    if (!aligned(vis->bits, 4) || !aligned(vis->rows, 8)) return DDTV_EINVAL;
+    return DDTV_OK;
+}
+
+struct Plan {
+    int path = DDTV_PATH_AUTO;
+    int rows_per_wg = 0;
+    int n_rt = 0;
+    int split_len = 0;
+    int n_split = 1;
+    int64_t grid = 0;
+    size_t ws_part_o = 0, ws_part_ml = 0, ws_bytes = 0;
+};
+
+// Estimated makespan (in tile-times) of a grid of workgroups dealt in order onto
+// `cus` compute units, one workgroup per CU at a time (both kernels use most of
+// a CU's LDS), plus the cost of the merge pass.
+double estimate(const std::vector<int>& kv, int n_rt, int L, int cus, double setup_tiles,
+                double merge_tiles_per_partial_row_split, int64_t R) {
+    std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+    for (int i = 0; i < cus; ++i) free_at.push(0.0);
+    double makespan = 0.0, merge = 0.0;
+    for (size_t b = 0; b < kv.size(); ++b) {
+        const int nb = (kv[b] + L - 1) / L;
+        for (int s = 0; s < nb; ++s) {
+            const int len = std::min(L, kv[b] - s * L);
+            const double cost = setup_tiles + (len + kTile - 1) / kTile;
+            for (int r = 0; r < n_rt; ++r) {
+                double t = free_at.top();
+                free_at.pop();
+                t += cost;
+                makespan = std::max(makespan, t);
+                free_at.push(t);
+            }
+        }
+        if (nb > 1) merge += merge_tiles_per_partial_row_split * (double)nb * (double)R;
+    }
+    return makespan + merge;
+}
+
+ddtv_status make_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const ddtv_opts* opts, Plan* p) {
+    ddtv_status st = check_vis(vis);
+    if (st) return st;
+    if (H < 1 || H > 65536) return DDTV_EINVAL;
+    if (kv_dtype != DDTV_F32 && kv_dtype != DDTV_BF16) return DDTV_EUNSUPPORTED;
+    const int path_req = opts ? opts->path : DDTV_PATH_AUTO;
+    if (path_req != DDTV_PATH_AUTO && path_req != DDTV_PATH_VALU && path_req != DDTV_PATH_MFMA)
+        return DDTV_EUNSUPPORTED;
+    const int split_req = opts ? opts->split_len : 0;
+    if (split_req < 0 || (split_req % kSplitQuantum) != 0) return DDTV_EINVAL;
+
+    p->path = path_req != DDTV_PATH_AUTO ? path_req : (vis->Q < 16 ? DDTV_PATH_VALU : DDTV_PATH_MFMA);
+    p->rows_per_wg = p->path == DDTV_PATH_MFMA ? kMfmaRows : kValuRows;
+    const int64_t R = (int64_t)vis->Q * H;
+    if (R > (int64_t)INT32_MAX / 2) return DDTV_EUNSUPPORTED;
+    p->n_rt = (int)((R + p->rows_per_wg - 1) / p->rows_per_wg);
+    const int max_kv = vis->max_kv;
+    const int single = (int)round_up((size_t)max_kv, kSplitQuantum);
+
+    if (split_req > 0) {
+        p->split_len = split_req;
+    } else {
+        std::vector<int> kv(vis->B);
+        for (int b = 0; b < vis->B; ++b)
+            kv[b] = vis->prefix_host ? vis->prefix_host[b] + vis->Q : max_kv;
+        const int cus = cu_count();
+        // Tile-time units: one 32-row cache tile through one workgroup.  A partial
+        // row costs 2 x 2 KiB of traffic in the merge (written, then read).
+        const bool mfma = p->path == DDTV_PATH_MFMA;
+        const double setup = mfma ? 2.0 : 1.0;
+        const double tile_us = mfma ? 7.3 : 1.0;
+        const double merge_per_row_split = (4096.0 / 4.0e12) * 1e6 / tile_us;   // ~4 TB/s effective
+        double best = 1e300;
+        int bestL = single;
+        const int64_t wg_cap = (int64_t)cus * 64;
+        for (int L = single;; L = (int)round_up((size_t)(L / 2), kSplitQuantum)) {
+            int64_t wgs = 0;
+            for (int b = 0; b < vis->B; ++b) wgs += (int64_t)((kv[b] + L - 1) / L) * p->n_rt;
+            if (wgs > wg_cap && L != single) break;
+            const double e = estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R);
+            if (e < best * 0.98) {   // prefer fewer splits unless clearly better
+                best = e;
+                bestL = L;
+            }
+            if (L <= 256) break;
+        }
+        p->split_len = bestL;
+    }
+    p->n_split = (max_kv + p->split_len - 1) / p->split_len;
+    p->grid = (int64_t)vis->B * p->n_rt * p->n_split;
+    if (p->grid > (int64_t)UINT32_MAX) return DDTV_EUNSUPPORTED;
+    if (p->n_split > 1) {
+        const size_t rows_total = (size_t)vis->B * p->n_split * (size_t)R;
+        p->ws_part_o = 0;
+        p->ws_part_ml = round_up(rows_total * kDLat * sizeof(float), 256);
+        p->ws_bytes = p->ws_part_ml + round_up(rows_total * sizeof(float2), 256);
+    } else {
+        p->ws_bytes = 0;
+    }
+    return DDTV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ddtv_version(void) { return kVersion; }
+
+const char* ddtv_status_string(ddtv_status s) {
+    switch (s) {
+        case DDTV_OK: return "ok";
+        case DDTV_EINVAL: return "invalid argument";
+        case DDTV_ETREE: return "malformed tree (parent array)";
+        case DDTV_EUNSUPPORTED: return "unsupported dtype, path or shape";
+        case DDTV_EWORKSPACE: return "workspace or visibility buffer too small";
+        case DDTV_EDEVICE: return "HIP device error";
+    }
+    return "unknown status";
+}
+
+size_t ddtv_vis_bytes(int32_t B, int32_t Q) {
+    if (B < 1 || Q < 1 || Q > kMaxQ) return 0;
+    return vis_layout(B, Q).total;
+}
+
+ddtv_status ddtv_build_visibility(const int32_t* parent, const int32_t* prefix_len, int32_t B, int32_t Q,
+                                  void* vis_buf, size_t vis_buf_bytes, ddtv_vis* vis, hipStream_t stream) {
+    if (!parent || !prefix_len || !vis_buf || !vis) return DDTV_EINVAL;
+    if (B < 1 || Q < 1 || Q > kMaxQ) return DDTV_EINVAL;
+    if (!aligned(parent, 4) || !aligned(vis_buf, 256)) return DDTV_EINVAL;
+    int64_t total = 0;
+    int32_t max_kv = 0;
+    for (int b = 0; b < B; ++b) {
+        if (prefix_len[b] < 0 || (int64_t)prefix_len[b] + Q > INT32_MAX) return DDTV_EINVAL;
+        total += (int64_t)prefix_len[b] + Q;
+        max_kv = std::max(max_kv, prefix_len[b] + Q);
+    }
+    const VisLayout L = vis_layout(B, Q);
+    if (vis_buf_bytes < L.total) return DDTV_EWORKSPACE;
+
+    char* base = static_cast<char*>(vis_buf);
+    ddtv_vis v{};
+    v.B = B;
+    v.Q = Q;
+    v.W = (Q + 31) / 32;
+    v.max_kv = max_kv;
+    v.total_kv = total;
+    v.bits = reinterpret_cast<uint32_t*>(base + L.bits);
+    v.rows = reinterpret_cast<ddtv_row*>(base + L.rows);
+    v.status = reinterpret_cast<int32_t*>(base + L.status);
+    v.prefix_host = prefix_len;
+
+    int64_t off = 0;
+    for (int b0 = 0; b0 < B; b0 += kVisChunk) {
+        const int nb = std::min(kVisChunk, B - b0);
+        VisChunk ch;
+        memset(&ch, 0, sizeof ch);
+        for (int k = 0; k < nb; ++k) {
+            ch.kv_off[k] = off;
+            ch.prefix[k] = prefix_len[b0 + k];
+            off += (int64_t)prefix_len[b0 + k] + Q;
+        }
+        if (launch_visibility(parent, b0, nb, Q, v.W, v.bits, v.rows, v.status, ch, stream) != hipSuccess)
+            return DDTV_EDEVICE;
+    }
+    *vis = v;
+    return DDTV_OK;
+}
+
+ddtv_status ddtv_read_status(const ddtv_vis* vis, int32_t* bad_row, int32_t* bad_node, hipStream_t stream) {
+    if (bad_row) *bad_row = -1;
+    if (bad_node) *bad_node = -1;
+    if (!vis || !vis->status || vis->B < 1) return DDTV_EINVAL;
+    std::vector<int32_t> st(vis->B);
+    if (hipStreamSynchronize(stream) != hipSuccess) return DDTV_EDEVICE;
+    if (hipMemcpy(st.data(), vis->status, sizeof(int32_t) * vis->B, hipMemcpyDeviceToHost) != hipSuccess)
+        return DDTV_EDEVICE;
+    for (int b = 0; b < vis->B; ++b) {
+        if (st[b] >= 0) {
+            if (bad_row) *bad_row = b;
+            if (bad_node) *bad_node = st[b];
+            return DDTV_ETREE;
+        }
+    }
+    return DDTV_OK;
+}
+
+size_t ddtv_workspace_bytes_ex(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const ddtv_opts* opts) {
+    Plan p;
+    if (make_plan(vis, H, kv_dtype, opts, &p) != DDTV_OK) return 0;
+    return p.ws_bytes;
+}
+
+size_t ddtv_workspace_bytes(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype) {
+    return ddtv_workspace_bytes_ex(vis, H, kv_dtype, nullptr);
+}
+
+ddtv_status ddtv_plan_info(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const ddtv_opts* opts,
+                           int32_t* path, int32_t* split_len, int32_t* n_split, int64_t* workgroups) {
+    Plan p;
+    ddtv_status st = make_plan(vis, H, kv_dtype, opts, &p);
+    if (st) return st;
+    if (path) *path = p.path;
+    if (split_len) *split_len = p.split_len;
+    if (n_split) *n_split = p.n_split;
+    if (workgroups) *workgroups = p.grid;
+    return DDTV_OK;
+}
+
+ddtv_status ddtv_verify_attn_ex(const float* q_abs, const float* q_rope, const void* ckv, const void* k_rope,
+                                ddtv_dtype kv_dtype, int32_t H, const ddtv_vis* vis, float scale, float* out,
+                                float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                const ddtv_opts* opts) {
+    if (!q_abs || !q_rope || !ckv || !k_rope || !out) return DDTV_EINVAL;
+    if (!aligned(q_abs, 16) || !aligned(q_rope, 16) || !aligned(ckv, 16) || !aligned(k_rope, 16) ||
+        !aligned(out, 16) || (lse && !aligned(lse, 4)))
+        return DDTV_EINVAL;
+    if (!isfinite(scale)) return DDTV_EINVAL;
+    Plan p;
+    ddtv_status st = make_plan(vis, H, kv_dtype, opts, &p);
+    if (st) return st;
+    if (p.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < p.ws_bytes) return DDTV_EWORKSPACE;
+        if (!aligned(workspace, 256)) return DDTV_EINVAL;
+    }
+
+    AttnArgs a;
+    a.q_abs = q_abs;
+    a.q_rope = q_rope;
+    a.ckv = ckv;
+    a.k_rope = k_rope;
+    a.bits = vis->bits;
+    a.rows = vis->rows;
+    a.out = out;
+    a.lse = lse;
+    a.part_o = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_part_o) : nullptr;
+    a.part_ml = p.ws_bytes ? reinterpret_cast<float2*>(static_cast<char*>(workspace) + p.ws_part_ml) : nullptr;
+    a.B = vis->B;
+    a.Q = vis->Q;
+    a.H = H;
+    a.W = vis->W;
+    a.R = vis->Q * H;
+    a.n_rt = p.n_rt;
+    a.split_len = p.split_len;
+    a.n_split = p.n_split;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+
+    if (opts && opts->attn_begin && hipEventRecord(opts->attn_begin, stream) != hipSuccess) return DDTV_EDEVICE;
+    hipError_t e = (p.path == DDTV_PATH_MFMA) ? launch_attn_mfma(a, kv_dtype, p.grid, stream)
+                                              : launch_attn_valu(a, kv_dtype, p.grid, stream);
+    if (e != hipSuccess) return DDTV_EDEVICE;
+    if (opts && opts->attn_end && hipEventRecord(opts->attn_end, stream) != hipSuccess) return DDTV_EDEVICE;
+    if (p.n_split > 1 && launch_merge(a, stream) != hipSuccess) return DDTV_EDEVICE;
+    return DDTV_OK;
+}
+
+ddtv_status ddtv_verify_attn(const float* q_abs, const float* q_rope, const void* ckv, const void* k_rope,
+                             ddtv_dtype kv_dtype, int32_t H, const ddtv_vis* vis, float scale, float* out,
+                             float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return ddtv_verify_attn_ex(q_abs, q_rope, ckv, k_rope, kv_dtype, H, vis, scale, out, lse, workspace,
+                               workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,352 @@
+// S2..S6 on the matrix cores -- the path for dense tree budgets (q_len >= 16).
+//
+// Same arithmetic as the VALU path (score = scale * (absorbed query . latent + rope
+// query . rope key), softmax over visible positions, weighted latent sum -- "The
+// Verify-Attn Kernel: A Single File Write ...", section "The Design Journey: From
+// Concept to CUDA"), organised for CDNA4 MFMA (v_mfma_f32_16x16x4_f32):
+//
+//  * A workgroup (8 waves) owns 64 query rows of one batch row and one KV split.
+//    All heads share one latent cache, so one LDS tile of 32 cache rows (576 floats
+//    each) feeds all 64 rows, and its first 512 columns serve as the value too:
+//    each cache row crosses HBM->LDS once per workgroup.
+//  * Waves come in pairs; a pair owns 16 query rows.  For the scores the pair
+//    splits the 576-long contraction (wave h holds query dims 288h .. 288h+287 in
+//    VGPRs for the whole split) and swaps partial sums through LDS; for the
+//    weighted sum it splits the 512 output dims (wave h accumulates dims
+//    256h .. 256h+255).  No MFMA is duplicated, and each wave needs ~half the
+//    registers a single owner of 16 rows would, which leaves room for two waves
+//    per SIMD.
+//  * Scores are produced transposed, S^T = K Q^T: the cache tile is the A operand,
+//    the query the B operand.  In that layout each lane holds probabilities of ONE
+//    query row, exactly the A-operand layout of P.V, so no shuffle is needed
+//    between the two contractions.  The contraction order is permuted the same way
+//    on both operands so every LDS operand fetch is a conflict-free 16-byte read.
+//  * Online softmax in exp2 units with lazy rescaling (the running max moves only
+//    when a tile beats it by more than 2^8).
+//  * fp32 caches go HBM->LDS with global_load_lds_dwordx4 (no VGPR staging),
+//    double buffered; bf16 caches are widened to fp32 through VGPRs on the way in.
+#include "ddtv_internal.hpp"
+
+namespace ddtv {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kRows = kMfmaRows;              // 64 query rows per workgroup
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTileChunks = kTile * kDQK / 4; // 4608 x 16 B per tile (72 KiB)
+
+// LDS tile layout (fp32, 16-byte chunks): a latent region of 32 rows x 128 chunks
+// followed by a rope region of 32 rows x 16 chunks.  Chunk c of row r is stored at
+// position c ^ (r & 15) of its row, so the 16 rows read together by an MFMA operand
+// fetch hit 16 different bank groups.
+constexpr int kRopeBase = kTile * 128;
+
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int lat_at(int r, int c) { return r * 128 + swz(r, c); }
+__device__ __forceinline__ int rope_at(int r, int c) { return kRopeBase + r * 16 + swz(r, c); }
+
+// fp32 cache straight into LDS.  Per wave: 8 instructions for the latent region
+// (half a row each, 1 KiB contiguous in HBM) and 1 for the rope region (4 rows x
+// 256 B).  Row indices and swizzle constants are wave-uniform; only the lane's
+// 16-byte column varies.
+__device__ __forceinline__ void issue_tile_f32(f32x4* buf, const AttnArgs& a, int64_t kv_base, int t0,
+                                               int kv_last, int wave, int lane) {
+    const float* ck = reinterpret_cast<const float*>(a.ckv);
+    const float* kr = reinterpret_cast<const float*>(a.k_rope);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int r = wave * 4 + (k >> 1);
+        const int p = (k & 1) * 64 + lane;
+        const int64_t row = kv_base + min(t0 + r, kv_last);
+        __builtin_amdgcn_global_load_lds(ck + row * kDLat + 4 * swz(r, p),
+                                         (lds_void*)(buf + r * 128 + (k & 1) * 64), 16, 0, 0);
+    }
+    {
+        const int r0 = wave * 4;
+        const int r = r0 + (lane >> 4);
+        const int64_t row = kv_base + min(t0 + r, kv_last);
+        __builtin_amdgcn_global_load_lds(kr + row * kDRope + 4 * swz(r, lane & 15),
+                                         (lds_void*)(buf + kRopeBase + r0 * 16), 16, 0, 0);
+    }
+}
+
+// bf16 cache: 16-byte loads (8 values) into VGPRs ...
+struct Bf16Stage {
+    uint4 v[5];
+};
+
+__device__ __forceinline__ void load_tile_bf16(Bf16Stage& st, const AttnArgs& a, int64_t kv_base, int t0,
+                                               int kv_last, int tid) {
+    const uint4* ck = reinterpret_cast<const uint4*>(a.ckv);
+    const uint4* kr = reinterpret_cast<const uint4*>(a.k_rope);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {   // latent: 32 rows x 64 pieces
+        const int r = k * 8 + (tid >> 6), c = tid & 63;
+        st.v[k] = ck[(kv_base + min(t0 + r, kv_last)) * 64 + c];
+    }
+    if (tid < 256) {                // rope: 32 rows x 8 pieces
+        const int r = tid >> 3, c = tid & 7;
+        st.v[4] = kr[(kv_base + min(t0 + r, kv_last)) * 8 + c];
+    }
+}
+
+// ... then widened and written to the swizzled fp32 layout.
+__device__ __forceinline__ void store_tile_bf16(f32x4* buf, const Bf16Stage& st, int tid) {
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+        if (k == 4 && tid >= 256) break;
+        const uint4 v = st.v[k];
+        const f32x4 lo = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+        const f32x4 hi = {bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        if (k < 4) {
+            const int r = k * 8 + (tid >> 6), c = tid & 63;
+            buf[lat_at(r, 2 * c)] = lo;
+            buf[lat_at(r, 2 * c + 1)] = hi;
+        } else {
+            const int r = tid >> 3, c = tid & 7;
+            buf[rope_at(r, 2 * c)] = lo;
+            buf[rope_at(r, 2 * c + 1)] = hi;
+        }
+    }
+}
+
+struct Smem {
+    f32x4 kv[2][kTileChunks];        // 2 x 72 KiB, double-buffered cache tile
+    float sx[kWaves][8][64];         // 16 KiB, partial scores swapped inside a wave pair
+};
+
+// One workgroup's work; HALF is the wave's half of the pair (wave-uniform).
+template <int KV_BF16, int HALF>
+__device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, int s, int rt, int wave,
+                                          int lane) {
+    const int tid = wave * 64 + lane;
+    const int g = lane >> 4;     // lane group
+    const int n = lane & 15;     // query row (score layout) within the pair's 16
+    const int pair = wave >> 1;
+
+    const ddtv_row rowd = a.rows[b];
+    const int kv_len = rowd.kv_len, P = rowd.prefix;
+    const int n_b = (kv_len + a.split_len - 1) / a.split_len;
+    const int kv_lo = s * a.split_len;
+    const int kv_hi = min(kv_len, kv_lo + a.split_len);
+    const int ntiles = (kv_hi - kv_lo + kTile - 1) / kTile;
+    const int64_t kv_base = rowd.kv_off;
+
+    Bf16Stage stage;
+    if (!KV_BF16)
+        issue_tile_f32(sm.kv[0], a, kv_base, kv_lo, kv_len - 1, wave, lane);
+    else
+        load_tile_bf16(stage, a, kv_base, kv_lo, kv_len - 1, tid);
+
+    // Query half: register t holds dims 16(18*HALF + t) + 4g .. +3 of row n (this
+    // permutation of the contraction index matches the cache-operand reads).
+    const int myrow = rt * kRows + pair * 16 + n;
+    const bool row_ok = myrow < a.R;
+    f32x4 qreg[18];
+    {
+        const int64_t qrow = (int64_t)b * a.R + (row_ok ? myrow : 0);
+        const f32x4* qa = reinterpret_cast<const f32x4*>(a.q_abs) + qrow * 128;
+        const f32x4* qr = reinterpret_cast<const f32x4*>(a.q_rope) + qrow * 16;
+#pragma unroll
+        for (int t = 0; t < 18; ++t) {
+            const int tg = 18 * HALF + t;
+            const f32x4 v = (tg < 32) ? qa[4 * tg + g] : qr[4 * (tg - 32) + g];
+            qreg[t] = row_ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    uint32_t mw[kMaxW];
+    {
+        const int q = row_ok ? myrow / a.H : 0;
+#pragma unroll
+        for (int k = 0; k < kMaxW; ++k) mw[k] = (k < a.W) ? a.bits[((int64_t)b * a.Q + q) * a.W + k] : 0u;
+    }
+
+    f32x4 oacc[16];   // output dims 256*HALF + 64T' + 4n + (c & 3) for block c = 4T' + (c & 3)
+#pragma unroll
+    for (int c = 0; c < 16; ++c) oacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;   // running max of row n (exp2 units)
+    float l_lane = 0.f;        // this lane's share of the running sum of row n
+
+    if (KV_BF16) store_tile_bf16(sm.kv[0], stage, tid);
+
+    for (int it = 0; it < ntiles; ++it) {
+        const int t0 = kv_lo + it * kTile;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();                                  // tile `it` is in LDS
+        const bool more = it + 1 < ntiles;
+        if (more) {
+            if (!KV_BF16)
+                issue_tile_f32(sm.kv[(it + 1) & 1], a, kv_base, t0 + kTile, kv_len - 1, wave, lane);
+            else
+                load_tile_bf16(stage, a, kv_base, t0 + kTile, kv_len - 1, tid);
+        }
+        const f32x4* K = sm.kv[it & 1];
+
+        // ---- partial S^T over this wave's half of the contraction; two
+        //      independent accumulators (cache rows n and 16 + n) interleaved.
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        {
+            auto kchunk = [&](int r, int t) -> f32x4 {
+                const int tg = 18 * HALF + t;
+                return (tg < 32) ? K[lat_at(r, 4 * tg + g)] : K[rope_at(r, 4 * (tg - 32) + g)];
+            };
+            f32x4 a0 = kchunk(n, 0), a1 = kchunk(16 + n, 0);
+#pragma unroll
+            for (int t = 0; t < 18; ++t) {
+                const f32x4 c0 = a0, c1 = a1;
+                if (t + 1 < 18) {
+                    a0 = kchunk(n, t + 1);
+                    a1 = kchunk(16 + n, t + 1);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(c0[u], qreg[t][u], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(c1[u], qreg[t][u], s1, 0, 0, 0);
+                }
+            }
+        }
+        // swap partial sums with the partner wave
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sm.sx[wave][e][lane] = s0[e];
+            sm.sx[wave][4 + e][lane] = s1[e];
+        }
+        __syncthreads();
+        float sv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sv[e] = s0[e] + sm.sx[wave ^ 1][e][lane];
+            sv[4 + e] = s1[e] + sm.sx[wave ^ 1][4 + e][lane];
+        }
+
+        // ---- online softmax; lane holds row n, cache rows (e>>2)*16 + 4g + (e&3)
+        const bool full = (t0 + kTile <= P) && (t0 + kTile <= kv_hi);
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = sv[e] * a.scale_log2;
+            if (!full) {
+                const int j = t0 + (e >> 2) * 16 + 4 * g + (e & 3);
+                bool vis = j < kv_hi;
+                if (vis && j >= P) vis = mask_bit(mw, j - P);
+                x = vis ? x : -INFINITY;
+            }
+            sv[e] = x;
+            tmax = fmaxf(tmax, x);
+        }
+        tmax = fmaxf(tmax, wave_xor(tmax, 16));
+        tmax = fmaxf(tmax, wave_xor(tmax, 32));
+        const bool raise = tmax > m_run + 8.f;
+        if (__any(raise)) {
+            const float m_new = raise ? tmax : m_run;
+            const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+            m_run = m_new;
+            l_lane *= alpha;
+            float aj[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) aj[j] = __shfl(alpha, 4 * g + j, 64);
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                oacc[c][0] *= aj[0];
+                oacc[c][1] *= aj[1];
+                oacc[c][2] *= aj[2];
+                oacc[c][3] *= aj[3];
+            }
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            sv[e] = exp2f(sv[e] - m_use);
+            l_lane += sv[e];
+        }
+
+        // ---- O += P V over this wave's 256 output dims
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int vr = (e >> 2) * 16 + 4 * g + (e & 3);
+            const float pv = sv[e];
+            f32x4 vf[4];
+#pragma unroll
+            for (int T = 0; T < 4; ++T) vf[T] = K[lat_at(vr, 16 * (4 * HALF + T) + n)];
+#pragma unroll
+            for (int T = 0; T < 4; ++T) {
+                oacc[4 * T + 0] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vf[T][0], oacc[4 * T + 0], 0, 0, 0);
+                oacc[4 * T + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vf[T][1], oacc[4 * T + 1], 0, 0, 0);
+                oacc[4 * T + 2] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vf[T][2], oacc[4 * T + 2], 0, 0, 0);
+                oacc[4 * T + 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vf[T][3], oacc[4 * T + 3], 0, 0, 0);
+            }
+        }
+
+        if (KV_BF16 && more) store_tile_bf16(sm.kv[(it + 1) & 1], stage, tid);
+    }
+
+    // ---- epilogue: output rows pair*16 + 4g + j of the tile, dims 256*HALF + 64T + 4n + (0..3)
+    float l_row = l_lane + wave_xor(l_lane, 16);
+    l_row += wave_xor(l_row, 32);
+    const float kLn2 = 0.69314718055994530942f;
+    const int orow_base = rt * kRows + pair * 16 + 4 * g;
+    if (n_b == 1) {
+        const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float ij = __shfl(inv, 4 * g + j, 64);
+            const int orow = orow_base + j;
+            if (orow < a.R) {
+                f32x4* dst = reinterpret_cast<f32x4*>(a.out) + ((int64_t)b * a.R + orow) * 128 + 64 * HALF;
+#pragma unroll
+                for (int T = 0; T < 4; ++T)
+                    dst[16 * T + n] = f32x4{oacc[4 * T + 0][j] * ij, oacc[4 * T + 1][j] * ij,
+                                            oacc[4 * T + 2][j] * ij, oacc[4 * T + 3][j] * ij};
+            }
+        }
+        if (HALF == 0 && a.lse && g == 0 && row_ok)
+            a.lse[(int64_t)b * a.R + myrow] = l_row > 0.f ? (m_run + log2f(l_row)) * kLn2 : -INFINITY;
+    } else {
+        const int64_t pbase = ((int64_t)b * a.n_split + s) * a.R;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int orow = orow_base + j;
+            if (orow < a.R) {
+                f32x4* dst = reinterpret_cast<f32x4*>(a.part_o) + (pbase + orow) * 128 + 64 * HALF;
+#pragma unroll
+                for (int T = 0; T < 4; ++T)
+                    dst[16 * T + n] = f32x4{oacc[4 * T + 0][j], oacc[4 * T + 1][j], oacc[4 * T + 2][j],
+                                            oacc[4 * T + 3][j]};
+            }
+        }
+        if (HALF == 0 && g == 0 && row_ok) a.part_ml[pbase + myrow] = make_float2(m_run, l_row);
+    }
+}
+
+template <int KV_BF16>
+__global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs a) {
+    __shared__ Smem sm;
+    const int64_t w = xcd_remap(blockIdx.x, gridDim.x);
+    const int rt = (int)(w % a.n_rt);
+    const int s = (int)((w / a.n_rt) % a.n_split);
+    const int b = (int)(w / ((int64_t)a.n_rt * a.n_split));
+    const int kv_len = a.rows[b].kv_len;
+    if (s * a.split_len >= kv_len) return;   // this batch row needs fewer splits
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (wave & 1)
+        attn_body<KV_BF16, 1>(a, sm, b, s, rt, wave, lane);
+    else
+        attn_body<KV_BF16, 0>(a, sm, b, s, rt, wave, lane);
+}
+
+}  // namespace
+
+hipError_t launch_attn_mfma(const AttnArgs& a, int kv_dtype, int64_t grid, hipStream_t stream) {
+    if (kv_dtype == DDTV_BF16)
+        hipLaunchKernelGGL(attn_mfma_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(attn_mfma_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace ddtv

@@ -1,0 +1,88 @@
+// Internal declarations shared by the HIP translation units of libddtv.
+// gfx950 (CDNA4) only: wave64, 160 KiB LDS per workgroup, MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ddtv.h"
+
+namespace ddtv {
+
+constexpr int kDLat = DDTV_D_LATENT;      // 512
+constexpr int kDRope = DDTV_D_ROPE;       // 64
+constexpr int kDQK = kDLat + kDRope;      // 576
+constexpr int kMaxQ = DDTV_MAX_Q;         // 256
+constexpr int kMaxW = kMaxQ / 32;         // 8 mask words
+constexpr int kTile = 32;                 // KV positions per LDS tile (both kernels)
+constexpr int kSplitQuantum = 64;         // split lengths are multiples of this
+constexpr int kVisChunk = 64;             // batch rows described per visibility launch
+constexpr int kXcds = 8;                  // MI355X: 8 XCDs, workgroups dealt round-robin
+
+// Everything the attention kernels need (passed by value).
+struct AttnArgs {
+    const float* q_abs;      // [B][Q][H][512]
+    const float* q_rope;     // [B][Q][H][64]
+    const void* ckv;         // [total_kv][512] f32 or bf16
+    const void* k_rope;      // [total_kv][64]
+    const uint32_t* bits;    // [B][Q][W]
+    const ddtv_row* rows;    // [B]
+    float* out;              // [B][Q][H][512]
+    float* lse;              // [B][Q][H] or null
+    float* part_o;           // [B][n_split][R][512]   (n_split > 1)
+    float2* part_ml;         // [B][n_split][R]  {m (log2 units), l}
+    int B, Q, H, W, R;       // R = Q*H query rows per batch row
+    int n_rt;                // row tiles per batch row
+    int split_len;           // KV positions per split (multiple of kSplitQuantum)
+    int n_split;             // splits per batch row in the grid (max over rows)
+    float scale_log2;        // scale * log2(e)
+};
+
+struct VisChunk {
+    int64_t kv_off[kVisChunk];
+    int32_t prefix[kVisChunk];
+};
+
+// Launchers (return the launch error, never synchronise).
+hipError_t launch_visibility(const int32_t* parent, int b0, int nb, int Q, int W, uint32_t* bits,
+                             ddtv_row* rows, int32_t* status, const VisChunk& chunk,
+                             hipStream_t stream);
+hipError_t launch_attn_valu(const AttnArgs& a, int kv_dtype, int64_t grid, hipStream_t stream);
+hipError_t launch_attn_mfma(const AttnArgs& a, int kv_dtype, int64_t grid, hipStream_t stream);
+hipError_t launch_merge(const AttnArgs& a, hipStream_t stream);
+
+constexpr int kValuRows = 16;   // query rows per VALU workgroup
+constexpr int kMfmaRows = 64;   // query rows per MFMA workgroup
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+#if defined(__HIPCC__)
+
+// Spread workgroup ids so that consecutive work items land on the same XCD
+// (the dispatcher deals workgroup i to XCD i % 8).  Bijective for any grid.
+__device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t G) {
+    const int64_t q = G / kXcds, r = G % kXcds;
+    const int64_t x = i % kXcds, k = i / kXcds;
+    return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// Wave-level butterflies (wave64).
+__device__ __forceinline__ float wave_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// Is tree column a (0 <= a < Q) set in a row's mask words?  w[] holds kMaxW words;
+// the index is dynamic, so select with a compare chain instead of scratch.
+__device__ __forceinline__ bool mask_bit(const uint32_t (&w)[kMaxW], int a) {
+    const int wi = a >> 5;
+    uint32_t word = w[0];
+#pragma unroll
+    for (int k = 1; k < kMaxW; ++k) word = (wi == k) ? w[k] : word;
+    return (word >> (a & 31)) & 1u;
+}
+
+#endif
+
+}  // namespace ddtv

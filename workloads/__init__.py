@@ -103,11 +103,31 @@ def tree_depths(parent: np.ndarray) -> np.ndarray:
 
 # --------------------------------------------------------------------------- tensors
 def round_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
+    """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even.
+    (Finite inputs only: the sum below cannot wrap for them.)"""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    lsb = (u >> 16) & 1
-    r = (u.astype(np.uint64) + 0x7FFF + lsb) >> 16
-    return r.astype(np.uint16)
+    r = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    return (r >> np.uint32(16)).astype(np.uint16)
+
+
+def _normal_rows(rng: np.random.Generator, rows: int, cols: int, sigma: float, bf16: bool,
+                 chunk_rows: int = 1 << 16) -> np.ndarray:
+    """rows x cols draws of N(0, sigma^2) as float32 (or bf16 bits), drawn in row
+    chunks: the stream of draws is the same as one big call, but a bf16 result
+    never holds the whole float32 array in memory."""
+    if not bf16:
+        a = rng.standard_normal((rows, cols), dtype=np.float32)
+        if sigma != 1.0:
+            a *= np.float32(sigma)
+        return a
+    out = np.empty((rows, cols), dtype=np.uint16)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        a = rng.standard_normal((r1 - r0, cols), dtype=np.float32)
+        if sigma != 1.0:
+            a *= np.float32(sigma)
+        out[r0:r1] = round_bf16_bits(a)
+    return out
 
 
 def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
@@ -153,13 +173,7 @@ class Workload:
         return w
 
 
-def make_workload(name: str, seed: int, B: int, H: int, Q: int, prefix,
-                  tree: str = "uniform", depth_cap: int = 0,
-                  q_sigma: float = 1.0, kv_sigma: float = 1.0,
-                  kv_dtype: int = F32, scale: float = SCALE_192) -> Workload:
-    """Draw one workload.  ``prefix`` is an int, a sequence of B ints, or a
-    (lo, hi) range given as ``("uniform", lo, hi)`` (inclusive)."""
-    rng = np.random.default_rng(seed)
+def _draw_trees(rng: np.random.Generator, B: int, Q: int, prefix, tree: str, depth_cap: int):
     # 1. trees
     if tree == "uniform":
         parent = np.stack([uniform_tree(rng, Q) for _ in range(B)])
@@ -176,6 +190,17 @@ def make_workload(name: str, seed: int, B: int, H: int, Q: int, prefix,
         pre = np.full(B, int(prefix), dtype=np.int32)
     else:
         pre = np.asarray(prefix, dtype=np.int32).reshape(B)
+    return parent.astype(np.int32), pre
+
+
+def make_workload(name: str, seed: int, B: int, H: int, Q: int, prefix,
+                  tree: str = "uniform", depth_cap: int = 0,
+                  q_sigma: float = 1.0, kv_sigma: float = 1.0,
+                  kv_dtype: int = F32, scale: float = SCALE_192) -> Workload:
+    """Draw one workload.  ``prefix`` is an int, a sequence of B ints, or a
+    (lo, hi) range given as ``("uniform", lo, hi)`` (inclusive)."""
+    rng = np.random.default_rng(seed)
+    parent, pre = _draw_trees(rng, B, Q, prefix, tree, depth_cap)
     total_kv = int((pre.astype(np.int64) + Q).sum())
     # 3. tensors
     q_abs = rng.standard_normal((B, Q, H, D_LATENT), dtype=np.float32)
@@ -184,15 +209,8 @@ def make_workload(name: str, seed: int, B: int, H: int, Q: int, prefix,
     q_rope = rng.standard_normal((B, Q, H, D_ROPE), dtype=np.float32)
     if q_sigma != 1.0:
         q_rope *= np.float32(q_sigma)
-    ckv = rng.standard_normal((total_kv, D_LATENT), dtype=np.float32)
-    if kv_sigma != 1.0:
-        ckv *= np.float32(kv_sigma)
-    k_rope = rng.standard_normal((total_kv, D_ROPE), dtype=np.float32)
-    if kv_sigma != 1.0:
-        k_rope *= np.float32(kv_sigma)
-    if kv_dtype == BF16:
-        ckv = round_bf16_bits(ckv)
-        k_rope = round_bf16_bits(k_rope)
+    ckv = _normal_rows(rng, total_kv, D_LATENT, kv_sigma, kv_dtype == BF16)
+    k_rope = _normal_rows(rng, total_kv, D_ROPE, kv_sigma, kv_dtype == BF16)
     return Workload(name=name, B=B, H=H, Q=Q, prefix=pre, parent=parent.astype(np.int32),
                     q_abs=q_abs, q_rope=q_rope, ckv=ckv, k_rope=k_rope,
                     kv_dtype=kv_dtype, scale=float(scale),
@@ -224,6 +242,15 @@ def config(name: str, seed: int | None = None, **override) -> Workload:
     kw = dict(CONFIGS[name])
     kw.update(override)
     return make_workload(name, 1000 + idx if seed is None else seed, **kw)
+
+
+def config_trees(name: str, seed: int | None = None):
+    """Only the trees and prefixes of a named workload (the first draws of its
+    stream), without drawing any tensor."""
+    idx = int(name[1:])
+    kw = dict(CONFIGS[name])
+    rng = np.random.default_rng(1000 + idx if seed is None else seed)
+    return _draw_trees(rng, kw["B"], kw["Q"], kw["prefix"], kw["tree"], kw.get("depth_cap", 0))
 
 
 def c2_chain() -> Workload:
