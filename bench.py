@@ -27,7 +27,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "tree-verify attn: achieved HBM GB/s (% of peak) and tree-query tokens/sec"
 HBM_PEAK_GBPS = 8000.0
-PEAK_TFLOPS = {"f32-mfma": 157.3, "bf16-mfma": 2500.0}
+# fp32 MFMA: 256 CU x 4 SIMD x 256 flop/clk/CU-equivalent at 2.4 GHz (published 157.3 TFLOP/s).
+# VALU without packed fp32: 256 CU x 64 lanes x 2 flop (FMA) x 2.4 GHz = 78.6 TFLOP/s.
+PEAK_TFLOPS = {"f32-mfma": 157.3, "bf16-mfma": 2500.0, "f32-valu": 78.6}
 KERNEL_SOURCES = ["attn_mfma.hip", "attn_valu.hip", "merge.hip", "visibility.hip", "api.hip",
                   "ddtv_internal.hpp"]
 
@@ -204,7 +206,8 @@ def main():
     tokens = w.B * w.Q
     value = tokens / (ms_step / 1e3)
     hbm_gbps = nbytes / (ms_step / 1e3) / 1e9
-    peak_key = "f32-mfma"       # the cache tile is widened to fp32 and contracted on fp32 MFMA
+    # the cache tile is held in fp32 in LDS and contracted on fp32 MFMA (or fp32 VALU FMAs)
+    peak_key = "f32-mfma" if path == dd.DDTV_PATH_MFMA else "f32-valu"
     achieved_tflops = flops / (attn_avg_ms / 1e3) / 1e12
     khash = kernel_source_hash()
     traffic = load_traffic(args.config, khash)
@@ -232,7 +235,7 @@ def main():
         "step_us": round(ms_step * 1e3, 2),
         "host_wall_ms_per_step": round((t_host1 - t_host0) * 1e3 / K, 4),
         "roofline": {
-            "bound": "mfma",
+            "bound": "mfma" if path == dd.DDTV_PATH_MFMA else "alu",
             "achieved": round(achieved_tflops, 3),
             "peak": PEAK_TFLOPS[peak_key],
             "unit": "TFLOP/s",
