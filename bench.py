@@ -30,7 +30,7 @@ HBM_PEAK_GBPS = 8000.0
 # fp32 MFMA: 256 CU x 4 SIMD x 256 flop/clk/CU-equivalent at 2.4 GHz (published 157.3 TFLOP/s).
 # VALU without packed fp32: 256 CU x 64 lanes x 2 flop (FMA) x 2.4 GHz = 78.6 TFLOP/s.
 PEAK_TFLOPS = {"f32-mfma": 157.3, "bf16-mfma": 2500.0, "f32-valu": 78.6}
-KERNEL_SOURCES = ["attn_mfma.hip", "attn_valu.hip", "merge.hip", "visibility.hip", "api.hip",
+KERNEL_SOURCES = ["attn_mfma.hip", "attn_mfma_bf16.hip", "attn_valu.hip", "merge.hip", "visibility.hip", "api.hip",
                   "ddtv_internal.hpp"]
 
 
@@ -138,7 +138,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
-    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
+    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA (cache precision), 3 fp32 MFMA")
     ap.add_argument("--split-len", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -206,8 +206,8 @@ def main():
     tokens = w.B * w.Q
     value = tokens / (ms_step / 1e3)
     hbm_gbps = nbytes / (ms_step / 1e3) / 1e9
-    # the cache tile is held in fp32 in LDS and contracted on fp32 MFMA (or fp32 VALU FMAs)
-    peak_key = "f32-mfma" if path == dd.DDTV_PATH_MFMA else "f32-valu"
+    bf16_mma = path == dd.DDTV_PATH_MFMA and w.kv_dtype == wl.BF16
+    peak_key = "bf16-mfma" if bf16_mma else ("f32-valu" if path == dd.DDTV_PATH_VALU else "f32-mfma")
     achieved_tflops = flops / (attn_avg_ms / 1e3) / 1e12
     khash = kernel_source_hash()
     traffic = load_traffic(args.config, khash)
@@ -223,7 +223,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if w.kv_dtype == wl.F32 else "bf16-kv/f32",
+        "dtype": "bf16" if bf16_mma else "f32",
         "data": "synthetic",
         "config": {"workload": f"{args.config}: {wl.DESCRIPTIONS[args.config]}", "B": w.B, "H": w.H,
                    "q_len": w.Q, "prefix": "ragged" if args.config == "c5" else int(w.prefix[0]),
@@ -235,13 +235,14 @@ def main():
         "step_us": round(ms_step * 1e3, 2),
         "host_wall_ms_per_step": round((t_host1 - t_host0) * 1e3 / K, 4),
         "roofline": {
-            "bound": "mfma" if path == dd.DDTV_PATH_MFMA else "alu",
+            "bound": "alu" if path == dd.DDTV_PATH_VALU else "mfma",
             "achieved": round(achieved_tflops, 3),
             "peak": PEAK_TFLOPS[peak_key],
             "unit": "TFLOP/s",
             "frac": round(achieved_tflops / PEAK_TFLOPS[peak_key], 4),
             "traffic": traffic,
-            "kernel": "attn_mfma_kernel" if path == 2 else "attn_valu_kernel",
+            "kernel": ("attn_mfma_bf16_kernel" if bf16_mma else
+                       "attn_valu_kernel" if path == dd.DDTV_PATH_VALU else "attn_mfma_kernel"),
             "flops_per_launch": flops,
             "algorithmic_bytes_per_step": nbytes,
             "visible_pairs": vis_pairs,

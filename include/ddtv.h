@@ -132,9 +132,13 @@ ddtv_status ddtv_read_status(const ddtv_vis *vis, int32_t *bad_row, int32_t *bad
 
 /* Execution path of the attention step. */
 typedef enum {
-    DDTV_PATH_AUTO = 0, /* VALU when Q < 16, MFMA otherwise */
-    DDTV_PATH_VALU = 1, /* vector-ALU kernel (any Q) */
-    DDTV_PATH_MFMA = 2  /* matrix-core kernel (any Q) */
+    DDTV_PATH_AUTO = 0,     /* VALU when Q < 16, MFMA otherwise */
+    DDTV_PATH_VALU = 1,     /* vector-ALU kernel, fp32 arithmetic (any Q) */
+    DDTV_PATH_MFMA = 2,     /* matrix-core kernel in the cache's precision (any Q): fp32 MFMA
+                               for fp32 caches; bf16 MFMA with fp32 accumulation for bf16
+                               caches (query and probabilities rounded to bf16) */
+    DDTV_PATH_MFMA_F32 = 3  /* fp32 MFMA for either cache dtype (bf16 widened exactly to
+                               fp32): slower on bf16 caches, fp32-accurate */
 } ddtv_path;
 
 /* Optional controls for ddtv_verify_attn_ex (zero-initialise for defaults). */

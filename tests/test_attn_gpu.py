@@ -67,11 +67,26 @@ def test_dense_reduced_f32():
     check_full(w, split_len=256, what="c4-small split256")
 
 
-def test_dense_reduced_bf16():
-    """c5's shape (H=64, q_len=64, uniform trees, bf16 cache) with short ragged prefixes."""
+@pytest.mark.parametrize("path", [0, 1, 3])
+def test_dense_reduced_bf16(path):
+    """c5's shape (H=64, q_len=64, uniform trees, bf16 cache) with short ragged prefixes,
+    on the bf16 matrix cores (auto), the VALU path and the fp32-MFMA path."""
     w = wl.make_workload("c5-small", 2005, B=3, H=64, Q=64, prefix=[0, 77, 700], tree="uniform",
                          kv_dtype=wl.BF16)
-    check_full(w)
+    r, out, lse = check_full(w, path=path)
+    if path != 0:
+        # the fp32-arithmetic paths on bf16 caches meet the fp32 bar as well
+        bits, _, _ = oracle.build_visibility(w.parent)
+        ref, _ = oracle_rows(w, bits)
+        assert_close(out, ref, 0, f"c5-small path {path} at the fp32 bar")
+    else:
+        assert r.plan()[1] == 2
+
+
+def test_bf16_mfma_split_and_ragged():
+    w = wl.make_workload("c5-split", 2006, B=2, H=64, Q=64, prefix=[1500, 333], tree="uniform",
+                         kv_dtype=wl.BF16)
+    check_full(w, split_len=256, what="bf16 split256")
 
 
 # ----------------------------------------------------------------------------- invariances
@@ -118,6 +133,21 @@ def test_edge_shapes(path, B, H, Q, prefix):
     check_full(w, path=path, what=f"edge B{B} H{H} Q{Q} P{prefix}")
 
 
+@pytest.mark.parametrize("B,H,Q,prefix", [
+    (1, 8, 1, [0]),
+    (2, 16, 1, [1000, 3]),
+    (1, 1, 256, [70]),
+    (2, 3, 40, [0, 33]),
+    (1, 16, 16, [0]),
+    (3, 5, 33, [31, 32, 95]),
+    (1, 64, 64, [129]),
+])
+def test_edge_shapes_bf16_mfma(B, H, Q, prefix):
+    w = wl.make_workload(f"edgeb{B}x{H}x{Q}", 5000 + B * 100 + Q, B=B, H=H, Q=Q, prefix=prefix,
+                         tree="uniform", kv_dtype=wl.BF16)
+    check_full(w, path=2, what=f"bf16 edge B{B} H{H} Q{Q} P{prefix}")
+
+
 @pytest.mark.parametrize("path", [1, 2])
 def test_single_visible_position_is_exact(path):
     """With no prefix the root sees only itself: p = 1, so the output is its latent row bit for bit."""
@@ -125,6 +155,16 @@ def test_single_visible_position_is_exact(path):
     r, out, lse = run(w, path=path)
     for h in range(w.H):
         assert np.array_equal(out[h], w.ckv[0]), h
+
+
+@pytest.mark.parametrize("path", [1, 2, 3])
+def test_single_visible_position_is_exact_bf16(path):
+    """Same on a bf16 cache: p = 1 is exact in bf16, so every path returns the widened row."""
+    w = wl.make_workload("c1-bf16", 1001, B=1, H=8, Q=9, prefix=0, tree="uniform", kv_dtype=wl.BF16)
+    r, out, lse = run(w, path=path)
+    row0 = wl.bf16_bits_to_f32(w.ckv[0])
+    for h in range(w.H):
+        assert np.array_equal(out[h], row0), h
 
 
 @pytest.mark.parametrize("path", [1, 2])

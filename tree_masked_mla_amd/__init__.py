@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libddtv.so")
 
 DDTV_OK, DDTV_EINVAL, DDTV_ETREE, DDTV_EUNSUPPORTED, DDTV_EWORKSPACE, DDTV_EDEVICE = range(6)
 DDTV_F32, DDTV_BF16 = 0, 1
-DDTV_PATH_AUTO, DDTV_PATH_VALU, DDTV_PATH_MFMA = 0, 1, 2
+DDTV_PATH_AUTO, DDTV_PATH_VALU, DDTV_PATH_MFMA, DDTV_PATH_MFMA_F32 = 0, 1, 2, 3
 D_LATENT, D_ROPE, MAX_Q = 512, 64, 256
 
 EXPORTED = (

@@ -58,6 +58,7 @@ ddtv_status check_vis(const ddtv_vis* vis) {
 
 struct Plan {
     int path = DDTV_PATH_AUTO;
+    bool bf16_mma = false;   // bf16 caches on the bf16 matrix cores
     int rows_per_wg = 0;
     int n_rt = 0;
     int split_len = 0;
@@ -98,13 +99,16 @@ ddtv_status make_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const
     if (H < 1 || H > 65536) return DDTV_EINVAL;
     if (kv_dtype != DDTV_F32 && kv_dtype != DDTV_BF16) return DDTV_EUNSUPPORTED;
     const int path_req = opts ? opts->path : DDTV_PATH_AUTO;
-    if (path_req != DDTV_PATH_AUTO && path_req != DDTV_PATH_VALU && path_req != DDTV_PATH_MFMA)
+    if (path_req != DDTV_PATH_AUTO && path_req != DDTV_PATH_VALU && path_req != DDTV_PATH_MFMA &&
+        path_req != DDTV_PATH_MFMA_F32)
         return DDTV_EUNSUPPORTED;
     const int split_req = opts ? opts->split_len : 0;
     if (split_req < 0 || (split_req % kSplitQuantum) != 0) return DDTV_EINVAL;
 
     p->path = path_req != DDTV_PATH_AUTO ? path_req : (vis->Q < 16 ? DDTV_PATH_VALU : DDTV_PATH_MFMA);
-    p->rows_per_wg = p->path == DDTV_PATH_MFMA ? kMfmaRows : kValuRows;
+    if (p->path == DDTV_PATH_MFMA_F32 && kv_dtype == DDTV_F32) p->path = DDTV_PATH_MFMA;
+    p->bf16_mma = p->path == DDTV_PATH_MFMA && kv_dtype == DDTV_BF16;
+    p->rows_per_wg = p->path == DDTV_PATH_VALU ? kValuRows : (p->bf16_mma ? bf16_rows_per_workgroup() : kMfmaRows);
     const int64_t R = (int64_t)vis->Q * H;
     if (R > (int64_t)INT32_MAX / 2) return DDTV_EUNSUPPORTED;
     p->n_rt = (int)((R + p->rows_per_wg - 1) / p->rows_per_wg);
@@ -120,9 +124,11 @@ ddtv_status make_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const
         const int cus = cu_count();
         // Tile-time units: one 32-row cache tile through one workgroup.  A partial
         // row costs 2 x 2 KiB of traffic in the merge (written, then read).
-        const bool mfma = p->path == DDTV_PATH_MFMA;
+        // tile_us: time of one tile through one workgroup at full rate (fp32 MFMA: 64 rows;
+        // bf16 MFMA: 128 rows at 16x the rate; VALU: 16 rows)
+        const bool mfma = p->path != DDTV_PATH_VALU;
         const double setup = mfma ? 2.0 : 1.0;
-        const double tile_us = mfma ? 7.3 : 1.0;
+        const double tile_us = p->bf16_mma ? 0.9 : (mfma ? 7.3 : 1.0);
         const double merge_per_row_split = (4096.0 / 4.0e12) * 1e6 / tile_us;   // ~4 TB/s effective
         double best = 1e300;
         int bestL = single;
@@ -300,8 +306,9 @@ ddtv_status ddtv_verify_attn_ex(const float* q_abs, const float* q_rope, const v
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 
     if (opts && opts->attn_begin && hipEventRecord(opts->attn_begin, stream) != hipSuccess) return DDTV_EDEVICE;
-    hipError_t e = (p.path == DDTV_PATH_MFMA) ? launch_attn_mfma(a, kv_dtype, p.grid, stream)
-                                              : launch_attn_valu(a, kv_dtype, p.grid, stream);
+    hipError_t e = p.bf16_mma ? launch_attn_mfma_bf16(a, p.grid, stream)
+                   : (p.path == DDTV_PATH_VALU) ? launch_attn_valu(a, kv_dtype, p.grid, stream)
+                                                : launch_attn_mfma(a, kv_dtype, p.grid, stream);
     if (e != hipSuccess) return DDTV_EDEVICE;
     if (opts && opts->attn_end && hipEventRecord(opts->attn_end, stream) != hipSuccess) return DDTV_EDEVICE;
     if (p.n_split > 1 && launch_merge(a, stream) != hipSuccess) return DDTV_EDEVICE;

@@ -342,6 +342,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn_mfma(const AttnArgs& a, int kv_dtype, int64_t grid, hipStream_t stream) {
+    (void)hipGetLastError();   // report only this launch's error
     if (kv_dtype == DDTV_BF16)
         hipLaunchKernelGGL(attn_mfma_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     else

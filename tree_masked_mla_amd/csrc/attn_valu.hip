@@ -189,6 +189,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn_valu(const AttnArgs& a, int kv_dtype, int64_t grid, hipStream_t stream) {
+    (void)hipGetLastError();   // report only this launch's error
     if (kv_dtype == DDTV_BF16)
         hipLaunchKernelGGL(attn_valu_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, a);
     else

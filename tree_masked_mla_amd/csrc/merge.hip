@@ -54,6 +54,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_merge(const AttnArgs& a, hipStream_t stream) {
+    (void)hipGetLastError();   // report only this launch's error
     const int64_t rows = (int64_t)a.B * a.R;
     hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0, stream, a);
     return hipGetLastError();

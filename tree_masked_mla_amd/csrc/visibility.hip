@@ -76,6 +76,7 @@ __global__ __launch_bounds__(256) void visibility_kernel(const int32_t* __restri
 hipError_t launch_visibility(const int32_t* parent, int b0, int nb, int Q, int W, uint32_t* bits,
                              ddtv_row* rows, int32_t* status, const VisChunk& chunk,
                              hipStream_t stream) {
+    (void)hipGetLastError();   // report only this launch's error
     hipLaunchKernelGGL(visibility_kernel, dim3(nb), dim3(256), 0, stream, parent, b0, Q, W, bits,
                        rows, status, chunk);
     return hipGetLastError();
