@@ -144,7 +144,7 @@ typedef enum {
 /* Optional controls for ddtv_verify_attn_ex (zero-initialise for defaults). */
 typedef struct {
     int32_t path;          /* ddtv_path */
-    int32_t split_len;     /* KV positions per split; 0 = automatic; else a multiple of 64 */
+    int32_t split_len;     /* KV positions per split; 0 = automatic; else a multiple of 32 */
     hipEvent_t attn_begin; /* if non-NULL: recorded on `stream` right before the main kernel */
     hipEvent_t attn_end;   /* if non-NULL: recorded on `stream` right after it (before the merge) */
 } ddtv_opts;

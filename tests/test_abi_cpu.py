@@ -114,7 +114,7 @@ def test_verify_host_errors(lib):
     assert verify_call(lib, vis, scale=float("inf")) == E
     assert verify_call(lib, vis, kv_dtype=2) == U
     assert verify_call(lib, vis, opts=dd.make_opts(path=4)) == U
-    assert verify_call(lib, vis, opts=dd.make_opts(split_len=100)) == E   # not a multiple of 64
+    assert verify_call(lib, vis, opts=dd.make_opts(split_len=100)) == E   # not a multiple of 32
     assert verify_call(lib, vis, opts=dd.make_opts(split_len=-64)) == E
     bad = fake_vis()
     bad.vis.W = 2

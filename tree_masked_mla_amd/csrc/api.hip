@@ -133,16 +133,23 @@ ddtv_status make_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const
         double best = 1e300;
         int bestL = single;
         const int64_t wg_cap = (int64_t)cus * 64;
-        for (int L = single;; L = (int)round_up((size_t)(L / 2), kSplitQuantum)) {
+        // Candidates: the longest row cut into S equal tile-aligned pieces, S = 1, 2, ...
+        // (stop once the grid is far beyond the device or pieces get short).
+        int prevL = 0;
+        for (int S = 1;; ++S) {
+            const int L = (int)round_up((size_t)((max_kv + S - 1) / S), kSplitQuantum);
+            if (L < 4 * kTile && S > 1) break;
+            if (L == prevL) continue;
+            prevL = L;
             int64_t wgs = 0;
             for (int b = 0; b < vis->B; ++b) wgs += (int64_t)((kv[b] + L - 1) / L) * p->n_rt;
-            if (wgs > wg_cap && L != single) break;
+            if (wgs > wg_cap && S > 1) break;
             const double e = estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R);
             if (e < best * 0.98) {   // prefer fewer splits unless clearly better
                 best = e;
                 bestL = L;
             }
-            if (L <= 256) break;
+            if (S >= 4096) break;
         }
         p->split_len = bestL;
     }

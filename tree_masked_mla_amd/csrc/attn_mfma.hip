@@ -119,6 +119,11 @@ struct Smem {
     float sx[kWaves][8][64];         // 16 KiB, partial scores swapped inside a wave pair
 };
 
+// Barrier after this wave's LDS writes have landed, leaving vector-memory loads
+// (the next tile's prefetch) in flight; the memory clobber keeps the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // One workgroup's work; HALF is the wave's half of the pair (wave-uniform).
 template <int KV_BF16, int HALF>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, int s, int rt, int wave,
@@ -158,12 +163,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
             qreg[t] = row_ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    uint32_t mw[kMaxW];
-    {
-        const int q = row_ok ? myrow / a.H : 0;
-#pragma unroll
-        for (int k = 0; k < kMaxW; ++k) mw[k] = (k < a.W) ? a.bits[((int64_t)b * a.Q + q) * a.W + k] : 0u;
-    }
+    // mask words of this lane's node, read only in the (few) tiles that reach the tree
+    const uint32_t* mrow = a.bits + ((int64_t)b * a.Q + (row_ok ? myrow / a.H : 0)) * a.W;
 
     f32x4 oacc[16];   // output dims 256*HALF + 64T' + 4n + (c & 3) for block c = 4T' + (c & 3)
 #pragma unroll
@@ -215,7 +216,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
             sm.sx[wave][e][lane] = s0[e];
             sm.sx[wave][4 + e][lane] = s1[e];
         }
-        __syncthreads();
+        if (KV_BF16)
+            __syncthreads();
+        else
+            lds_barrier();   // the fp32 tile prefetch (LDS DMA) stays in flight
         float sv[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -232,7 +236,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
             if (!full) {
                 const int j = t0 + (e >> 2) * 16 + 4 * g + (e & 3);
                 bool vis = j < kv_hi;
-                if (vis && j >= P) vis = mask_bit(mw, j - P);
+                if (vis && j >= P) vis = (mrow[(j - P) >> 5] >> ((j - P) & 31)) & 1u;
                 x = vis ? x : -INFINITY;
             }
             sv[e] = x;
