@@ -30,8 +30,12 @@ HBM_PEAK_GBPS = 8000.0
 # fp32 MFMA: 256 CU x 4 SIMD x 256 flop/clk/CU-equivalent at 2.4 GHz (published 157.3 TFLOP/s).
 # VALU without packed fp32: 256 CU x 64 lanes x 2 flop (FMA) x 2.4 GHz = 78.6 TFLOP/s.
 PEAK_TFLOPS = {"f32-mfma": 157.3, "bf16-mfma": 2500.0, "f32-valu": 78.6}
-KERNEL_SOURCES = ["attn_mfma.hip", "attn_mfma_bf16.hip", "attn_valu.hip", "merge.hip", "visibility.hip", "api.hip",
-                  "ddtv_internal.hpp"]
+# sources of each kernel whose PMC traffic may be quoted (the hash ties counters to code)
+KERNEL_SOURCES = {
+    "attn_mfma_kernel": ["attn_mfma.hip", "ddtv_internal.hpp"],
+    "attn_mfma_bf16_kernel": ["attn_mfma_bf16.hip", "ddtv_internal.hpp"],
+    "attn_valu_kernel": ["attn_valu.hip", "ddtv_internal.hpp"],
+}
 
 
 def log(msg):
@@ -86,9 +90,9 @@ def algorithmic(w):
     return nbytes, flops, vis_pairs
 
 
-def kernel_source_hash():
+def kernel_source_hash(kernel):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "tree_masked_mla_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -209,7 +213,9 @@ def main():
     bf16_mma = path == dd.DDTV_PATH_MFMA and w.kv_dtype == wl.BF16
     peak_key = "bf16-mfma" if bf16_mma else ("f32-valu" if path == dd.DDTV_PATH_VALU else "f32-mfma")
     achieved_tflops = flops / (attn_avg_ms / 1e3) / 1e12
-    khash = kernel_source_hash()
+    kernel = ("attn_mfma_bf16_kernel" if bf16_mma else
+              "attn_valu_kernel" if path == dd.DDTV_PATH_VALU else "attn_mfma_kernel")
+    khash = kernel_source_hash(kernel)
     traffic = load_traffic(args.config, khash)
 
     out = {
@@ -241,8 +247,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved_tflops / PEAK_TFLOPS[peak_key], 4),
             "traffic": traffic,
-            "kernel": ("attn_mfma_bf16_kernel" if bf16_mma else
-                       "attn_valu_kernel" if path == dd.DDTV_PATH_VALU else "attn_mfma_kernel"),
+            "kernel": kernel,
             "flops_per_launch": flops,
             "algorithmic_bytes_per_step": nbytes,
             "visible_pairs": vis_pairs,

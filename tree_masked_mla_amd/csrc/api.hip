@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <functional>
+#include <mutex>
 #include <queue>
 #include <vector>
 
@@ -93,7 +94,70 @@ double estimate(const std::vector<int>& kv, int n_rt, int L, int cus, double set
     return makespan + merge;
 }
 
+ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const ddtv_opts* opts,
+                               Plan* p);
+
+// Plans are pure functions of the shapes, the options, the device's CU count and
+// the per-row cache lengths; a verify loop re-plans the same shapes every step, so
+// the last few plans are kept (the split search simulates a schedule and is too
+// slow to repeat per call).
+struct PlanKey {
+    int32_t B, Q, W, max_kv, H, dtype, path, split, cus;
+    int64_t total_kv;
+    uint64_t prefix_hash;
+    bool operator==(const PlanKey& o) const { return memcmp(this, &o, sizeof *this) == 0; }
+};
+
+uint64_t hash_prefix(const ddtv_vis* vis) {
+    uint64_t h = 1469598103934665603ull;   // FNV-1a over the prefix lengths
+    if (!vis->prefix_host) return h;
+    for (int b = 0; b < vis->B; ++b) {
+        h ^= (uint32_t)vis->prefix_host[b];
+        h *= 1099511628211ull;
+    }
+    return h;
+}
+
 ddtv_status make_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const ddtv_opts* opts, Plan* p) {
+    ddtv_status st = check_vis(vis);
+    if (st) return st;
+    PlanKey key;
+    memset(&key, 0, sizeof key);
+    key.B = vis->B;
+    key.Q = vis->Q;
+    key.W = vis->W;
+    key.max_kv = vis->max_kv;
+    key.total_kv = vis->total_kv;
+    key.H = H;
+    key.dtype = kv_dtype;
+    key.path = opts ? opts->path : 0;
+    key.split = opts ? opts->split_len : 0;
+    key.cus = cu_count();
+    key.prefix_hash = hash_prefix(vis);
+    static std::mutex mu;
+    static PlanKey keys[8];
+    static Plan plans[8];
+    static int used = 0, next = 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < used; ++i)
+            if (keys[i] == key) {
+                *p = plans[i];
+                return DDTV_OK;
+            }
+    }
+    st = make_plan_uncached(vis, H, kv_dtype, opts, p);
+    if (st) return st;
+    std::lock_guard<std::mutex> lock(mu);
+    keys[next] = key;
+    plans[next] = *p;
+    next = (next + 1) % 8;
+    if (used < 8) ++used;
+    return DDTV_OK;
+}
+
+ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const ddtv_opts* opts,
+                               Plan* p) {
     ddtv_status st = check_vis(vis);
     if (st) return st;
     if (H < 1 || H > 65536) return DDTV_EINVAL;
@@ -108,7 +172,7 @@ ddtv_status make_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const
     p->path = path_req != DDTV_PATH_AUTO ? path_req : (vis->Q < 16 ? DDTV_PATH_VALU : DDTV_PATH_MFMA);
     if (p->path == DDTV_PATH_MFMA_F32 && kv_dtype == DDTV_F32) p->path = DDTV_PATH_MFMA;
     p->bf16_mma = p->path == DDTV_PATH_MFMA && kv_dtype == DDTV_BF16;
-    p->rows_per_wg = p->path == DDTV_PATH_VALU ? kValuRows : (p->bf16_mma ? bf16_rows_per_workgroup() : kMfmaRows);
+    p->rows_per_wg = p->path == DDTV_PATH_VALU ? kValuRows : (p->bf16_mma ? bf16_rows_per_workgroup() : mfma_rows_per_workgroup(kv_dtype));
     const int64_t R = (int64_t)vis->Q * H;
     if (R > (int64_t)INT32_MAX / 2) return DDTV_EUNSUPPORTED;
     p->n_rt = (int)((R + p->rows_per_wg - 1) / p->rows_per_wg);
@@ -135,7 +199,7 @@ ddtv_status make_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const
         const int64_t wg_cap = (int64_t)cus * 64;
         // Candidates: the longest row cut into S equal tile-aligned pieces, S = 1, 2, ...
         // (stop once the grid is far beyond the device or pieces get short).
-        int prevL = 0;
+        int prevL = 0, worse = 0;
         for (int S = 1;; ++S) {
             const int L = (int)round_up((size_t)((max_kv + S - 1) / S), kSplitQuantum);
             if (L < 4 * kTile && S > 1) break;
@@ -148,6 +212,9 @@ ddtv_status make_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const
             if (e < best * 0.98) {   // prefer fewer splits unless clearly better
                 best = e;
                 bestL = L;
+                worse = 0;
+            } else if (wgs > 2 * (int64_t)cus && ++worse >= 8) {
+                break;               // past a full device and no longer improving
             }
             if (S >= 4096) break;
         }

@@ -34,7 +34,7 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kRows = kMfmaRows;              // 64 query rows per workgroup
+constexpr int kRows = 64;                     // query rows per workgroup
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTileChunks = kTile * kDQK / 4; // 4608 x 16 B per tile (72 KiB)
@@ -119,11 +119,6 @@ struct Smem {
     float sx[kWaves][8][64];         // 16 KiB, partial scores swapped inside a wave pair
 };
 
-// Barrier after this wave's LDS writes have landed, leaving vector-memory loads
-// (the next tile's prefetch) in flight; the memory clobber keeps the compiler
-// from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // One workgroup's work; HALF is the wave's half of the pair (wave-uniform).
 template <int KV_BF16, int HALF>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, int s, int rt, int wave,
@@ -163,8 +158,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
             qreg[t] = row_ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    // mask words of this lane's node, read only in the (few) tiles that reach the tree
-    const uint32_t* mrow = a.bits + ((int64_t)b * a.Q + (row_ok ? myrow / a.H : 0)) * a.W;
+    uint32_t mw[kMaxW];
+    {
+        const int q = row_ok ? myrow / a.H : 0;
+#pragma unroll
+        for (int k = 0; k < kMaxW; ++k) mw[k] = (k < a.W) ? a.bits[((int64_t)b * a.Q + q) * a.W + k] : 0u;
+    }
 
     f32x4 oacc[16];   // output dims 256*HALF + 64T' + 4n + (c & 3) for block c = 4T' + (c & 3)
 #pragma unroll
@@ -216,10 +215,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
             sm.sx[wave][e][lane] = s0[e];
             sm.sx[wave][4 + e][lane] = s1[e];
         }
-        if (KV_BF16)
-            __syncthreads();
-        else
-            lds_barrier();   // the fp32 tile prefetch (LDS DMA) stays in flight
+        __syncthreads();
         float sv[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -236,7 +232,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
             if (!full) {
                 const int j = t0 + (e >> 2) * 16 + 4 * g + (e & 3);
                 bool vis = j < kv_hi;
-                if (vis && j >= P) vis = (mrow[(j - P) >> 5] >> ((j - P) & 31)) & 1u;
+                if (vis && j >= P) vis = mask_bit(mw, j - P);
                 x = vis ? x : -INFINITY;
             }
             sv[e] = x;
@@ -344,6 +340,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs a) {
 }
 
 }  // namespace
+
+int mfma_rows_per_workgroup(int /*kv_dtype*/) { return kRows; }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, int kv_dtype, int64_t grid, hipStream_t stream) {
     (void)hipGetLastError();   // report only this launch's error

@@ -49,12 +49,12 @@ hipError_t launch_visibility(const int32_t* parent, int b0, int nb, int Q, int W
                              hipStream_t stream);
 hipError_t launch_attn_valu(const AttnArgs& a, int kv_dtype, int64_t grid, hipStream_t stream);
 hipError_t launch_attn_mfma(const AttnArgs& a, int kv_dtype, int64_t grid, hipStream_t stream);
+int mfma_rows_per_workgroup(int kv_dtype);   // query rows per workgroup of the fp32 MFMA kernel
 hipError_t launch_attn_mfma_bf16(const AttnArgs& a, int64_t grid, hipStream_t stream);
 int bf16_rows_per_workgroup();   // query rows per workgroup of the bf16 MFMA kernel
 hipError_t launch_merge(const AttnArgs& a, hipStream_t stream);
 
 constexpr int kValuRows = 16;   // query rows per VALU workgroup
-constexpr int kMfmaRows = 64;   // query rows per fp32-MFMA workgroup
 
 // ---------------------------------------------------------------------------
 // Device helpers
