@@ -188,8 +188,8 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
         const int cus = cu_count();
         // Tile-time units: one 32-row cache tile through one workgroup.  A partial
         // row costs 2 x 2 KiB of traffic in the merge (written, then read).
-        // tile_us: time of one tile through one workgroup at full rate (fp32 MFMA: 64 rows;
-        // bf16 MFMA: 128 rows at 16x the rate; VALU: 16 rows)
+        // tile_us: rough time of one tile through one workgroup (fp32 MFMA and bf16
+        // MFMA: 64 rows; VALU: 16 rows)
         const bool mfma = p->path != DDTV_PATH_VALU;
         const double setup = mfma ? 2.0 : 1.0;
         const double tile_us = p->bf16_mma ? 0.9 : (mfma ? 7.3 : 1.0);

@@ -10,15 +10,15 @@
 // weighted sum; every product is accumulated in fp32 and the softmax statistics
 // are fp32.
 //
-// Organisation (4 waves = 2 wave pairs per workgroup, 64 query rows):
-//  * A wave pair owns 32 query rows (two 16-row blocks) of one batch row and KV
-//    split.  For the scores the pair splits the 576-long contraction (wave h keeps
-//    query dims 288h .. 288h+287 of its 32 rows in VGPRs as bf16) and swaps partial
-//    sums through LDS; for P.V it splits the 512 output dims (wave h accumulates
-//    dims 256h .. 256h+255 of the 32 rows).  No MFMA is duplicated, and every cache
-//    fragment read from LDS feeds two MFMAs (one per row block): LDS instruction
-//    issue, not the matrix cores, is what limits a bf16 kernel on this chip, so the
-//    reuse matters more than occupancy (a wave needs ~300 registers: one per SIMD).
+// Organisation (the launched geometry: 8 waves = 4 wave pairs, 64 query rows per
+// workgroup, one workgroup per CU):
+//  * A wave pair owns 16 query rows of one batch row and KV split.  For the scores
+//    the pair splits the 576-long contraction (wave h keeps query dims 288h ..
+//    288h+287 of its rows in 36 VGPRs as bf16) and swaps partial sums through LDS;
+//    for P.V it splits the 512 output dims (wave h accumulates dims 256h ..
+//    256h+255).  No MFMA is duplicated; 196 VGPRs, two waves per SIMD.  The
+//    template also builds 32 rows per pair (RB = 2: every cache fragment read from
+//    LDS feeds two MFMAs), which needs one wave per SIMD and ran slower.
 //  * Scores are produced transposed, S^T = K Q^T: A = 16 cache rows x 32 dims read
 //    from LDS (16 bytes per lane), B = the query fragment in VGPRs.  Each lane then
 //    holds the scores of ONE query row for 8 cache positions -- the A-operand
@@ -32,8 +32,8 @@
 //    units so both the score reads and the transpose reads spread over the banks.
 //    Every per-lane LDS offset is computed once; inside the loop only the tile
 //    base changes, and block / dim selection folds into instruction offsets.
-//  * Tiles arrive with global_load_lds_dwordx4 into a ring of 4 buffers, 3 tiles
-//    ahead.  Barriers are raw s_barrier with only the waits they need (the
+//  * Tiles arrive with global_load_lds_dwordx4 into a ring of 4 buffers (144 KiB),
+//    3 tiles ahead.  Barriers are raw s_barrier with only the waits they need (the
 //    loop-top one waits for the oldest tile alone, the score-swap one for LDS
 //    only), so prefetches stay in flight across them.
 //  * Row maxima cross lanes with v_permlane32_swap / v_permlane16_swap (no LDS).
