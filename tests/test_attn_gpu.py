@@ -89,6 +89,17 @@ def test_bf16_mfma_split_and_ragged():
     check_full(w, split_len=256, what="bf16 split256")
 
 
+@pytest.mark.parametrize("split_len", [32, 64, 96])
+def test_bf16_mfma_short_splits(split_len):
+    """Splits of one, two and three 32-position tiles: the bf16 kernel's slot
+    pipeline has separate start-up and drain steps for each count (plus the
+    merge over many partials)."""
+    w = wl.make_workload("c5-short", 2007, B=2, H=8, Q=24, prefix=[5, 70], tree="uniform",
+                         kv_dtype=wl.BF16)
+    r, _, _ = check_full(w, path=2, split_len=split_len, what=f"bf16 split{split_len}")
+    assert r.plan()[2] == split_len
+
+
 # ----------------------------------------------------------------------------- invariances
 def test_split_count_invariance():
     w = wl.config("c3")

@@ -10,12 +10,16 @@
 //
 // 128 threads per query row (one float4 of the 512-d output each), 2 rows per
 // workgroup.  Rows whose batch row needed a single split were finished by the
-// attention kernel and are skipped.
+// attention kernel and are skipped.  The split statistics and partial outputs are
+// read in batches of kBatch independent loads, so a row costs a few memory round
+// trips instead of two per split.
 #include "ddtv_internal.hpp"
 
 namespace ddtv {
 
 namespace {
+
+constexpr int kBatch = 8;
 
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
     const int64_t gr = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);   // b * R + row
@@ -28,22 +32,40 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
     if (n_b <= 1) return;
     const int c = threadIdx.x & 127;
     const int64_t pbase = (int64_t)b * a.n_split * a.R + row;   // split s at pbase + s * R
+    const float4* po = reinterpret_cast<const float4*>(a.part_o);
 
     float M = -INFINITY;
-    for (int s = 0; s < n_b; ++s) M = fmaxf(M, a.part_ml[pbase + (int64_t)s * a.R].x);
+    for (int s0 = 0; s0 < n_b; s0 += kBatch) {
+        float mx[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+            mx[k] = (s0 + k < n_b) ? a.part_ml[pbase + (int64_t)(s0 + k) * a.R].x : -INFINITY;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) M = fmaxf(M, mx[k]);
+    }
     float L = 0.f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     if (M != -INFINITY) {
-        for (int s = 0; s < n_b; ++s) {
-            const float2 ml = a.part_ml[pbase + (int64_t)s * a.R];
-            if (ml.x == -INFINITY) continue;
-            const float wgt = exp2f(ml.x - M);
-            L += wgt * ml.y;
-            const float4 v = reinterpret_cast<const float4*>(a.part_o)[(pbase + (int64_t)s * a.R) * 128 + c];
-            o.x = fmaf(wgt, v.x, o.x);
-            o.y = fmaf(wgt, v.y, o.y);
-            o.z = fmaf(wgt, v.z, o.z);
-            o.w = fmaf(wgt, v.w, o.w);
+        for (int s0 = 0; s0 < n_b; s0 += kBatch) {
+            float2 ml[kBatch];
+            float4 v[kBatch];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const bool in = s0 + k < n_b;
+                const int64_t p = pbase + (int64_t)(in ? s0 + k : 0) * a.R;
+                ml[k] = in ? a.part_ml[p] : make_float2(-INFINITY, 0.f);
+                v[k] = in ? po[p * 128 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                // an empty split (m = -inf) has l = 0 and o = 0: weight 0
+                const float wgt = (ml[k].x == -INFINITY) ? 0.f : exp2f(ml[k].x - M);
+                L = fmaf(wgt, ml[k].y, L);
+                o.x = fmaf(wgt, v[k].x, o.x);
+                o.y = fmaf(wgt, v[k].y, o.y);
+                o.z = fmaf(wgt, v[k].z, o.z);
+                o.w = fmaf(wgt, v[k].w, o.w);
+            }
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
