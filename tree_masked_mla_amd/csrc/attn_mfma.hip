@@ -49,6 +49,15 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 15); }
 __device__ __forceinline__ int lat_at(int r, int c) { return r * 128 + swz(r, c); }
 __device__ __forceinline__ int rope_at(int r, int c) { return kRopeBase + r * 16 + swz(r, c); }
 
+// max over the 4 lanes holding one query row (lanes l, l^16, l^32, l^48), with
+// lane swaps on the vector ALU instead of LDS permutes
+__device__ __forceinline__ float row_max4(float x) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(x, fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(x, fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1])));
+}
+
 // fp32 cache straight into LDS.  Per wave: 8 instructions for the latent region
 // (half a row each, 1 KiB contiguous in HBM) and 1 for the rope region (4 rows x
 // 256 B).  Row indices and swizzle constants are wave-uniform; only the lane's
@@ -143,7 +152,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         load_tile_bf16(stage, a, kv_base, kv_lo, kv_len - 1, tid);
 
     // Query half: register t holds dims 16(18*HALF + t) + 4g .. +3 of row n (this
-    // permutation of the contraction index matches the cache-operand reads).
+    // permutation of the contraction index matches the cache-operand reads),
+    // pre-multiplied by scale*log2(e) so the scores come out in exp2 units.
     const int myrow = rt * kRows + pair * 16 + n;
     const bool row_ok = myrow < a.R;
     f32x4 qreg[18];
@@ -155,7 +165,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         for (int t = 0; t < 18; ++t) {
             const int tg = 18 * HALF + t;
             const f32x4 v = (tg < 32) ? qa[4 * tg + g] : qr[4 * (tg - 32) + g];
-            qreg[t] = row_ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+            qreg[t] = row_ok ? v * a.scale_log2 : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
     uint32_t mw[kMaxW];
@@ -228,7 +238,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         float tmax = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            float x = sv[e] * a.scale_log2;
+            float x = sv[e];
             if (!full) {
                 const int j = t0 + (e >> 2) * 16 + 4 * g + (e & 3);
                 bool vis = j < kv_hi;
@@ -238,12 +248,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
             sv[e] = x;
             tmax = fmaxf(tmax, x);
         }
-        tmax = fmaxf(tmax, wave_xor(tmax, 16));
-        tmax = fmaxf(tmax, wave_xor(tmax, 32));
+        tmax = row_max4(tmax);
         const bool raise = tmax > m_run + 8.f;
         if (__any(raise)) {
             const float m_new = raise ? tmax : m_run;
-            const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
             l_lane *= alpha;
             float aj[4];
@@ -260,7 +269,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            sv[e] = exp2f(sv[e] - m_use);
+            sv[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
             l_lane += sv[e];
         }
 
