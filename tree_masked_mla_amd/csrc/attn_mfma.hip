@@ -21,6 +21,12 @@
 //    query row, exactly the A-operand layout of P.V, so no shuffle is needed
 //    between the two contractions.  The contraction order is permuted the same way
 //    on both operands so every LDS operand fetch is a conflict-free 16-byte read.
+//    The swizzle reduces to 4 per-lane base offsets per operand kind plus
+//    compile-time immediates (TileOffsets); addressing it that way instead of
+//    through the swizzle function leaves the register allocator ~20 VGPRs and made
+//    the kernel ~2 % faster.
+//  * Row maxima cross lanes with permlane swaps; exponentials are the raw v_exp_f32;
+//    the query is pre-scaled by scale*log2(e) when it is loaded.
 //  * Online softmax in exp2 units with lazy rescaling (the running max moves only
 //    when a tile beats it by more than 2^8).
 //  * fp32 caches go HBM->LDS with global_load_lds_dwordx4 (no VGPR staging),
@@ -128,6 +134,133 @@ struct Smem {
     float sx[kWaves][8][64];         // 16 KiB, partial scores swapped inside a wave pair
 };
 
+// Per-lane byte offsets inside a tile buffer, derived from the swizzle (chunk c
+// of row r at c ^ (r & 15)); with them every operand read is one register plus
+// a compile-time immediate.  Lane (g, n), x = g ^ (n & 3), y = (n >> 2) & 3:
+//  score operand, latent step tg = 4a + b, cache row n:  qoff[b] + 256 a   (row 16+n: +32 KiB)
+//  score operand, rope step 32 + t, cache row n:          roff[t]           (row 16+n: +4 KiB)
+//  value operand, cache row 16h + 4g + j, dims 16 blk + n: voff[j] + 256 blk (h = 1: +32 KiB)
+struct TileOffsets {
+    uint32_t qoff[4], roff[4], voff[4];
+};
+
+__device__ __forceinline__ TileOffsets tile_offsets(int g, int n) {
+    TileOffsets o;
+    const int x = g ^ (n & 3), y = (n >> 2) & 3;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        o.qoff[b] = n * 2048 + ((b ^ y) << 6) + (x << 4);
+        o.roff[b] = kRopeBase * 16 + n * 256 + ((b ^ y) << 6) + (x << 4);
+        o.voff[b] = (4 * g + b) * 2048 + ((n ^ (4 * g + b)) << 4);
+    }
+    return o;
+}
+
+__device__ __forceinline__ f32x4 lds16(const char* base, uint32_t off) {
+    return *reinterpret_cast<const f32x4*>(base + off);
+}
+
+// Partial S^T of the tile at Kb over this wave's half of the contraction (two
+// independent accumulators: cache rows n and 16 + n), stored to the wave's swap area.
+template <int HALF>
+__device__ __forceinline__ void qk_slot(const char* Kb, const TileOffsets& to, const f32x4 (&qreg)[18],
+                                        float* sx_mine, int lane) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    auto kchunk = [&](int row_hi, int t) -> f32x4 {
+        const int tg = 18 * HALF + t;
+        return (tg < 32) ? lds16(Kb, to.qoff[tg & 3] + 256 * (tg >> 2) + row_hi * 32768)
+                         : lds16(Kb, to.roff[tg - 32] + row_hi * 4096);
+    };
+    f32x4 a0 = kchunk(0, 0), a1 = kchunk(1, 0);
+#pragma unroll
+    for (int t = 0; t < 18; ++t) {
+        const f32x4 c0 = a0, c1 = a1;
+        if (t + 1 < 18) {
+            a0 = kchunk(0, t + 1);
+            a1 = kchunk(1, t + 1);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(c0[u], qreg[t][u], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(c1[u], qreg[t][u], s1, 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        sx_mine[e * 64 + lane] = s0[e];
+        sx_mine[(4 + e) * 64 + lane] = s1[e];
+    }
+}
+
+// Full scores of the tile starting at cache position t0 (own partial and the
+// partner's, both from LDS), online softmax, then O += P V over this wave's 256 dims.
+template <int HALF>
+__device__ __forceinline__ void sm_pv_slot(f32x4 (&oacc)[16], const float* sx_mine, const float* sx_partner,
+                                           const char* Kb, const TileOffsets& to, float& m_run, float& l_lane,
+                                           const uint32_t* mrow, int g, int n, int lane, int t0, int P,
+                                           int kv_hi) {
+    float sv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        sv[e] = sx_mine[e * 64 + lane] + sx_partner[e * 64 + lane];
+        sv[4 + e] = sx_mine[(4 + e) * 64 + lane] + sx_partner[(4 + e) * 64 + lane];
+    }
+    const bool full = (t0 + kTile <= P) && (t0 + kTile <= kv_hi);
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float x = sv[e];
+        if (!full) {
+            const int j = t0 + (e >> 2) * 16 + 4 * g + (e & 3);
+            bool vis = j < kv_hi;
+            if (vis && j >= P) vis = (mrow[(j - P) >> 5] >> ((j - P) & 31)) & 1u;
+            x = vis ? x : -INFINITY;
+        }
+        sv[e] = x;
+        tmax = fmaxf(tmax, x);
+    }
+    tmax = row_max4(tmax);
+    const bool raise = tmax > m_run + 8.f;
+    if (__any(raise)) {
+        const float m_new = raise ? tmax : m_run;
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_lane *= alpha;
+        float aj[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) aj[j] = __shfl(alpha, 4 * g + j, 64);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            oacc[c][0] *= aj[0];
+            oacc[c][1] *= aj[1];
+            oacc[c][2] *= aj[2];
+            oacc[c][3] *= aj[3];
+        }
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        sv[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
+        l_lane += sv[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int vr = (e >> 2) * 16 + 4 * g + (e & 3);
+        const float pv = sv[e];
+        f32x4 vf[4];
+#pragma unroll
+        for (int T = 0; T < 4; ++T) vf[T] = lds16(Kb, to.voff[e & 3] + (e >> 2) * 32768 + 256 * (4 * HALF + T));
+        (void)vr;
+#pragma unroll
+        for (int T = 0; T < 4; ++T) {
+            oacc[4 * T + 0] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vf[T][0], oacc[4 * T + 0], 0, 0, 0);
+            oacc[4 * T + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vf[T][1], oacc[4 * T + 1], 0, 0, 0);
+            oacc[4 * T + 2] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vf[T][2], oacc[4 * T + 2], 0, 0, 0);
+            oacc[4 * T + 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vf[T][3], oacc[4 * T + 3], 0, 0, 0);
+        }
+    }
+}
+
 // One workgroup's work; HALF is the wave's half of the pair (wave-uniform).
 template <int KV_BF16, int HALF>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, int s, int rt, int wave,
@@ -168,13 +301,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
             qreg[t] = row_ok ? v * a.scale_log2 : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    uint32_t mw[kMaxW];
-    {
-        const int q = row_ok ? myrow / a.H : 0;
-#pragma unroll
-        for (int k = 0; k < kMaxW; ++k) mw[k] = (k < a.W) ? a.bits[((int64_t)b * a.Q + q) * a.W + k] : 0u;
-    }
-
+    // mask words of this row's node (read only in the tiles that reach the tree)
+    const uint32_t* mrow = a.bits + ((int64_t)b * a.Q + (row_ok ? myrow / a.H : 0)) * a.W;
     f32x4 oacc[16];   // output dims 256*HALF + 64T' + 4n + (c & 3) for block c = 4T' + (c & 3)
 #pragma unroll
     for (int c = 0; c < 16; ++c) oacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -183,113 +311,24 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
 
     if (KV_BF16) store_tile_bf16(sm.kv[0], stage, tid);
 
+    const TileOffsets to = tile_offsets(g, n);
+    float* sx_mine = &sm.sx[wave][0][0];
+    const float* sx_partner = &sm.sx[wave ^ 1][0][0];
     for (int it = 0; it < ntiles; ++it) {
-        const int t0 = kv_lo + it * kTile;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();                                  // tile `it` is in LDS
         const bool more = it + 1 < ntiles;
         if (more) {
             if (!KV_BF16)
-                issue_tile_f32(sm.kv[(it + 1) & 1], a, kv_base, t0 + kTile, kv_len - 1, wave, lane);
+                issue_tile_f32(sm.kv[(it + 1) & 1], a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, wave, lane);
             else
-                load_tile_bf16(stage, a, kv_base, t0 + kTile, kv_len - 1, tid);
+                load_tile_bf16(stage, a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, tid);
         }
-        const f32x4* K = sm.kv[it & 1];
-
-        // ---- partial S^T over this wave's half of the contraction; two
-        //      independent accumulators (cache rows n and 16 + n) interleaved.
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-        {
-            auto kchunk = [&](int r, int t) -> f32x4 {
-                const int tg = 18 * HALF + t;
-                return (tg < 32) ? K[lat_at(r, 4 * tg + g)] : K[rope_at(r, 4 * (tg - 32) + g)];
-            };
-            f32x4 a0 = kchunk(n, 0), a1 = kchunk(16 + n, 0);
-#pragma unroll
-            for (int t = 0; t < 18; ++t) {
-                const f32x4 c0 = a0, c1 = a1;
-                if (t + 1 < 18) {
-                    a0 = kchunk(n, t + 1);
-                    a1 = kchunk(16 + n, t + 1);
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(c0[u], qreg[t][u], s0, 0, 0, 0);
-                    s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(c1[u], qreg[t][u], s1, 0, 0, 0);
-                }
-            }
-        }
-        // swap partial sums with the partner wave
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sm.sx[wave][e][lane] = s0[e];
-            sm.sx[wave][4 + e][lane] = s1[e];
-        }
-        __syncthreads();
-        float sv[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sv[e] = s0[e] + sm.sx[wave ^ 1][e][lane];
-            sv[4 + e] = s1[e] + sm.sx[wave ^ 1][4 + e][lane];
-        }
-
-        // ---- online softmax; lane holds row n, cache rows (e>>2)*16 + 4g + (e&3)
-        const bool full = (t0 + kTile <= P) && (t0 + kTile <= kv_hi);
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = sv[e];
-            if (!full) {
-                const int j = t0 + (e >> 2) * 16 + 4 * g + (e & 3);
-                bool vis = j < kv_hi;
-                if (vis && j >= P) vis = mask_bit(mw, j - P);
-                x = vis ? x : -INFINITY;
-            }
-            sv[e] = x;
-            tmax = fmaxf(tmax, x);
-        }
-        tmax = row_max4(tmax);
-        const bool raise = tmax > m_run + 8.f;
-        if (__any(raise)) {
-            const float m_new = raise ? tmax : m_run;
-            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_lane *= alpha;
-            float aj[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) aj[j] = __shfl(alpha, 4 * g + j, 64);
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                oacc[c][0] *= aj[0];
-                oacc[c][1] *= aj[1];
-                oacc[c][2] *= aj[2];
-                oacc[c][3] *= aj[3];
-            }
-        }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            sv[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
-            l_lane += sv[e];
-        }
-
-        // ---- O += P V over this wave's 256 output dims
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int vr = (e >> 2) * 16 + 4 * g + (e & 3);
-            const float pv = sv[e];
-            f32x4 vf[4];
-#pragma unroll
-            for (int T = 0; T < 4; ++T) vf[T] = K[lat_at(vr, 16 * (4 * HALF + T) + n)];
-#pragma unroll
-            for (int T = 0; T < 4; ++T) {
-                oacc[4 * T + 0] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vf[T][0], oacc[4 * T + 0], 0, 0, 0);
-                oacc[4 * T + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vf[T][1], oacc[4 * T + 1], 0, 0, 0);
-                oacc[4 * T + 2] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vf[T][2], oacc[4 * T + 2], 0, 0, 0);
-                oacc[4 * T + 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vf[T][3], oacc[4 * T + 3], 0, 0, 0);
-            }
-        }
-
+        const char* Kb = reinterpret_cast<const char*>(sm.kv[it & 1]);
+        qk_slot<HALF>(Kb, to, qreg, sx_mine, lane);
+        __syncthreads();                                  // partner's partial scores are in LDS
+        sm_pv_slot<HALF>(oacc, sx_mine, sx_partner, Kb, to, m_run, l_lane, mrow, g, n, lane, kv_lo + it * kTile, P,
+                         kv_hi);
         if (KV_BF16 && more) store_tile_bf16(sm.kv[(it + 1) & 1], stage, tid);
     }
 
