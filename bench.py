@@ -14,6 +14,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import hashlib
+import re
 import json
 import os
 import platform
@@ -90,11 +91,17 @@ def algorithmic(w):
     return nbytes, flops, vis_pairs
 
 
+_COMMENTS = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
 def kernel_source_hash(kernel):
+    """First 16 hex digits of a sha256 over the kernel's sources with comments, blank
+    lines and trailing blanks removed: the recorded traffic depends on the code only."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "tree_masked_mla_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "tree_masked_mla_amd", "csrc", f)) as fh:
+            code = _COMMENTS.sub("", fh.read())
+        h.update("\n".join(l.rstrip() for l in code.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 
@@ -144,6 +151,9 @@ def main():
     ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA (cache precision), 3 fp32 MFMA")
     ap.add_argument("--split-len", type=int, default=0)
+    ap.add_argument("--q-len", type=int, default=0,
+                    help="override the workload's tree size (probe runs, e.g. q_len 1 = decode); "
+                         "not the benchmarked configuration")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0,
@@ -165,8 +175,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    log(f"generating {args.config}: {wl.DESCRIPTIONS[args.config]}")
-    w = wl.config(args.config)
+    desc = wl.DESCRIPTIONS[args.config]
+    if args.q_len:
+        desc += f" [probe: q_len overridden to {args.q_len}]"
+    log(f"generating {args.config}: {desc}")
+    w = wl.config(args.config, Q=args.q_len) if args.q_len else wl.config(args.config)
 
     if args.copy_calibration:
         nbytes = w.ckv.nbytes
@@ -216,7 +229,7 @@ def main():
     kernel = ("attn_mfma_bf16_kernel" if bf16_mma else
               "attn_valu_kernel" if path == dd.DDTV_PATH_VALU else "attn_mfma_kernel")
     khash = kernel_source_hash(kernel)
-    traffic = load_traffic(args.config, khash)
+    traffic = None if args.q_len else load_traffic(args.config, khash)
 
     out = {
         "metric": METRIC,
@@ -231,7 +244,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if bf16_mma else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{args.config}: {wl.DESCRIPTIONS[args.config]}", "B": w.B, "H": w.H,
+        "config": {"workload": f"{args.config}: {desc}", "B": w.B, "H": w.H,
                    "q_len": w.Q, "prefix": "ragged" if args.config == "c5" else int(w.prefix[0]),
                    "total_kv_rows": w.total_kv, "scale": w.scale, "path": path, "split_len": split_len,
                    "n_split": n_split, "workgroups": wgs},

@@ -132,7 +132,9 @@ ddtv_status ddtv_read_status(const ddtv_vis *vis, int32_t *bad_row, int32_t *bad
 
 /* Execution path of the attention step. */
 typedef enum {
-    DDTV_PATH_AUTO = 0,     /* VALU when Q < 16, MFMA otherwise */
+    DDTV_PATH_AUTO = 0,     /* VALU when a batch row has fewer than 16 query rows (Q * H < 16),
+                               MFMA otherwise: all heads share the latent cache, so the Q * H
+                               rows of a batch row contract against each cache tile together */
     DDTV_PATH_VALU = 1,     /* vector-ALU kernel, fp32 arithmetic (any Q) */
     DDTV_PATH_MFMA = 2,     /* matrix-core kernel in the cache's precision (any Q): fp32 MFMA
                                for fp32 caches; bf16 MFMA with fp32 accumulation for bf16

@@ -136,12 +136,13 @@ def test_verify_host_errors(lib):
 
 
 def test_plan_rules(lib):
-    # q_len < 16 -> VALU, else MFMA; forced paths honoured
-    for Q, want in [(1, dd.DDTV_PATH_VALU), (9, dd.DDTV_PATH_VALU), (15, dd.DDTV_PATH_VALU),
-                    (16, dd.DDTV_PATH_MFMA), (128, dd.DDTV_PATH_MFMA)]:
+    # fewer than 16 query rows per batch row (Q * H) -> VALU, else MFMA; forced paths honoured
+    for Q, H, want in [(1, 8, dd.DDTV_PATH_VALU), (1, 15, dd.DDTV_PATH_VALU), (15, 1, dd.DDTV_PATH_VALU),
+                       (1, 16, dd.DDTV_PATH_MFMA), (16, 1, dd.DDTV_PATH_MFMA), (9, 8, dd.DDTV_PATH_MFMA),
+                       (128, 16, dd.DDTV_PATH_MFMA)]:
         vis = fake_vis(B=1, Q=Q, prefix=(100,))
-        rc, path, L, ns, wg = dd.ddtv_plan_info(vis, 8, 0)
-        assert rc == 0 and path == want
+        rc, path, L, ns, wg = dd.ddtv_plan_info(vis, H, 0)
+        assert rc == 0 and path == want, (Q, H, path)
     vis = fake_vis(B=1, Q=9, prefix=(100,))
     assert dd.ddtv_plan_info(vis, 8, 0, dd.make_opts(path=dd.DDTV_PATH_MFMA))[1] == dd.DDTV_PATH_MFMA
     # a forced split length gives ceil(max_kv / L) splits and a matching workspace

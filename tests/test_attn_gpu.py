@@ -123,9 +123,9 @@ def test_path_invariance():
     _, o_mfma, _ = check_full(w, path=2)
     _, o_valu, _ = check_full(w, path=1)
     assert np.abs(o_mfma - o_valu).max() < 1e-5
-    assert run(w)[0].plan()[1] == 2      # auto picks MFMA at q_len = 16
-    w15 = wl.make_workload("q15", 3015, B=1, H=8, Q=15, prefix=[40], tree="uniform")
-    assert run(w15)[0].plan()[1] == 1    # and VALU below it
+    assert run(w)[0].plan()[1] == 2      # auto: 128 query rows per batch row -> MFMA
+    w15 = wl.make_workload("q15", 3015, B=1, H=1, Q=15, prefix=[40], tree="uniform")
+    assert run(w15)[0].plan()[1] == 1    # and VALU below 16 rows
 
 
 # ----------------------------------------------------------------------------- edge cases

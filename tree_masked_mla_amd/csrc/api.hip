@@ -169,7 +169,12 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     const int split_req = opts ? opts->split_len : 0;
     if (split_req < 0 || (split_req % kSplitQuantum) != 0) return DDTV_EINVAL;
 
-    p->path = path_req != DDTV_PATH_AUTO ? path_req : (vis->Q < 16 ? DDTV_PATH_VALU : DDTV_PATH_MFMA);
+    // Auto: the matrix cores once a batch row's query rows fill a 16-row MFMA tile.
+    // All heads share the latent cache, so the H * Q rows of a batch row contract
+    // against every cache tile together; the vector-ALU kernel is kept for the
+    // cases with fewer rows than that.
+    p->path = path_req != DDTV_PATH_AUTO ? path_req
+                                         : ((int64_t)vis->Q * H < kValuRows ? DDTV_PATH_VALU : DDTV_PATH_MFMA);
     if (p->path == DDTV_PATH_MFMA_F32 && kv_dtype == DDTV_F32) p->path = DDTV_PATH_MFMA;
     p->bf16_mma = p->path == DDTV_PATH_MFMA && kv_dtype == DDTV_BF16;
     p->rows_per_wg = p->path == DDTV_PATH_VALU ? kValuRows : (p->bf16_mma ? bf16_rows_per_workgroup() : mfma_rows_per_workgroup(kv_dtype));

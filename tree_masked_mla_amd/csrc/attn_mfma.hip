@@ -1,4 +1,4 @@
-// S2..S6 on the matrix cores -- the path for dense tree budgets (q_len >= 16).
+// S2..S6 on the matrix cores -- the path once a batch row has 16 or more query rows (H * q_len).
 //
 // Same arithmetic as the VALU path (score = scale * (absorbed query . latent + rope
 // query . rope key), softmax over visible positions, weighted latent sum -- "The

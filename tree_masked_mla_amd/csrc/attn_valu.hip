@@ -1,4 +1,4 @@
-// S2..S6 on the vector ALUs -- the path for sparse trees (q_len < 16).
+// S2..S6 on the vector ALUs -- the path for batch rows with fewer than 16 query rows (H * q_len < 16).
 //
 // Score = scale * (absorbed query . latent + rope query . rope key); softmax over
 // the node's visible positions; output = weighted sum of latents ("The Verify-Attn
