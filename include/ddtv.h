@@ -27,7 +27,11 @@
  *     without touching the device.  Device-side launch failures map to
  *     DDTV_EDEVICE.  No exception crosses this interface.
  *   - Device pointers to float data must be 16-byte aligned.
- *   - Calls are stateless and re-entrant; calls on different streams may overlap.
+ *   - Calls are re-entrant and thread-safe; calls on different streams may overlap
+ *     (each with its own output and workspace buffers).  The only state kept is a
+ *     small cache of split plans (keyed by shapes, options, CU count and prefix
+ *     lengths, guarded by a lock) and the per-device CU count; neither changes
+ *     results.
  */
 #ifndef DDTV_H
 #define DDTV_H

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert dd.ddtv_version() == 100
+    assert dd.ddtv_version() == 200
     for code in range(6):
         assert dd.ddtv_status_string(code)
     assert dd.ddtv_status_string(2).startswith("malformed tree")
@@ -185,3 +185,25 @@ def test_oracle_shares_error_contract(lib):
     assert rc == oracle.REF_EINVAL == dd.DDTV_EINVAL
     b, _, rc = oracle.build_visibility(np.array([[0, 0]], np.int32))
     assert rc == oracle.REF_ETREE == dd.DDTV_ETREE
+
+
+def test_plan_cache_is_thread_safe(lib):
+    """Plans come from a small shared cache (more shapes than entries here, so
+    entries are evicted while other threads read): every thread must get exactly
+    the plan a lone caller gets, and repeated calls must agree."""
+    from concurrent.futures import ThreadPoolExecutor
+    shapes = [(B, Q, H, tuple(int(p) for p in np.random.default_rng(B * 1000 + Q).integers(0, 40000, B)))
+              for B in (1, 3, 8) for Q in (16, 64, 128) for H in (8, 16, 64)]
+    keep = {}
+
+    def plan(shape):
+        B, Q, H, prefix = shape
+        vis = fake_vis(B=B, Q=Q, prefix=prefix)
+        keep[shape] = vis                 # the borrowed prefix array must outlive the call
+        return dd.ddtv_plan_info(vis, H, 0)
+
+    expected = {s: plan(s) for s in shapes}
+    with ThreadPoolExecutor(8) as ex:
+        for _ in range(3):
+            got = list(ex.map(plan, shapes * 4))
+            assert got == [expected[s] for s in shapes * 4]

@@ -17,7 +17,7 @@ using namespace ddtv;
 
 namespace {
 
-constexpr int32_t kVersion = 100;   // 0.1.0
+constexpr int32_t kVersion = 200;   // 0.2.0: automatic path by query rows per batch row
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
