@@ -219,6 +219,12 @@ template <int HALF, bool PV, bool QK>
 __device__ __forceinline__ void mfma_slot(f32x4 (&oacc)[16], f32x4 (&sa)[2], const bf16x8& pa, const bf16x8 (&qreg)[9],
                                           const uint32_t (&toff)[8], const uint32_t (&koff)[6], uint32_t kb_pv,
                                           uint32_t kb_qk, f32x4* sx_mine, int lane) {
+    uint32_t ka[6];
+    f32x4 k0[6], k1[6];
+    if constexpr (QK) {
+#pragma unroll
+        for (int k = 0; k < 6; ++k) ka[k] = kb_qk + koff[k];
+    }
     if constexpr (PV) {
         uint32_t va[8];
 #pragma unroll
@@ -234,16 +240,20 @@ __device__ __forceinline__ void mfma_slot(f32x4 (&oacc)[16], f32x4 (&sa)[2], con
         tr_batch<HALF, 12>(v1, va);
         lgkm_wait_tied<8>(v0);
         pv_batch<8>(oacc, pa, v0);
-        lgkm_wait_tied<0>(v1);
-        pv_batch<12>(oacc, pa, v1);
+        if constexpr (QK) {
+            // the first score-operand batch goes out before the last P.V batch
+            k_batch<9 * HALF + 0>(k0, ka);          // in flight: v1 (8) + k0 (6)
+            lgkm_wait_tied<6>(v1);
+            pv_batch<12>(oacc, pa, v1);
+        } else {
+            lgkm_wait_tied<0>(v1);
+            pv_batch<12>(oacc, pa, v1);
+        }
+    } else if constexpr (QK) {
+        k_batch<9 * HALF + 0>(k0, ka);
     }
     if constexpr (QK) {
-        uint32_t ka[6];
-#pragma unroll
-        for (int k = 0; k < 6; ++k) ka[k] = kb_qk + koff[k];
-        f32x4 k0[6], k1[6];
         sa[0] = sa[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        k_batch<9 * HALF + 0>(k0, ka);
         k_batch<9 * HALF + 3>(k1, ka);
         lgkm_wait_tied<6>(k0);
         qk_batch<0>(sa, qreg, k0);
@@ -377,8 +387,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
     f32x4* sx_mine = &sm.sx[wave][0][0];
     const f32x4* sx_partner = &sm.sx[wave ^ 1][0][0];
     auto buf = [&](int t) { return ring0 + (uint32_t)(t & (kRing - 1)) * kBufBytes; };
-    // Tile m goes into the buffer of tile m-4, whose last reader (group 1's P.V)
-    // finished in the slot before.
+    // Tile m goes into the buffer of tile m-4, whose last reader (group 1's P.V of
+    // tile m-4) ran in slot 2m-5.  Each wave issues its share of a tile during its
+    // softmax slot, where the issue cost is hidden behind the other group's MFMAs:
+    // group 1 in slot 2m-4, group 0 in slot 2m-3.
     auto issue = [&](int m) {
         if (m < ntiles) issue_tile(sm.kv[m & (kRing - 1)], a, kv_base, kv_lo + m * kTile, kv_len - 1, wave, lane);
     };
@@ -394,15 +406,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
     // Slots: group 0 runs "MFMA slot t, softmax slot t" in slots 2t, 2t+1; group 1
     // runs the same one slot later.  The MFMA slot of tile t does the P.V of tile
     // t-1 and the partial scores of tile t; one slot after the last tile, the P.V
-    // of the last tile.  Tile m is issued in slot 2m-4 (tiles 0, 1 before the loop).
+    // of the last tile.  Tiles 0 and 1 are issued before the loop.
     if (grp == 0) {
         for (int t = 0; t < ntiles; ++t) {
-            issue(t + 2);                                                   // slot 2t
             if (t == 0)
                 mfma_slot<HALF, false, true>(oacc, sa, pa, qreg, toff, koff, 0, buf(t), sx_mine, lane);
             else
                 mfma_slot<HALF, true, true>(oacc, sa, pa, qreg, toff, koff, buf(t - 1), buf(t), sx_mine, lane);
-            slot_barrier();
+            slot_barrier();                                                 // slot 2t
+            issue(t + 2);
             softmax_slot(oacc, sa, pa, m_run, l_lane, sx_partner, lane, kv_lo + t * kTile, P, kv_hi, mrow);
             end_odd_slot(t + 1);                                            // slot 2t+1
         }
