@@ -39,7 +39,9 @@
 //  * LDS: latent rows of 1024 B and rope rows of 128 B, XOR-swizzled in 32-byte
 //    units so both the score reads and the transpose reads spread over the banks.
 //    Tiles arrive with global_load_lds_dwordx4 into a ring of 4 buffers (144 KiB),
-//    two tiles (four slots) ahead; 16 KiB hold the partial scores.
+//    issued three to four slots before first use, each wave's share in its
+//    softmax slot (issuing them costs a few hundred cycles, which an MFMA slot
+//    would pay on its critical path); 16 KiB hold the partial scores.
 //  * Row maxima cross lanes with v_permlane32_swap / v_permlane16_swap (no LDS).
 #include "ddtv_internal.hpp"
 
