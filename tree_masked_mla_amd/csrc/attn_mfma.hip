@@ -161,10 +161,11 @@ __device__ __forceinline__ f32x4 lds16(const char* base, uint32_t off) {
 }
 
 // Partial S^T of the tile at Kb over this wave's half of the contraction (two
-// independent accumulators: cache rows n and 16 + n), stored to the wave's swap area.
-template <int HALF>
+// independent accumulators: cache rows n and 16 + n), stored to the wave's swap
+// area; issue() starts the next tile's loads part-way through.
+template <int HALF, class Issue>
 __device__ __forceinline__ void qk_slot(const char* Kb, const TileOffsets& to, const f32x4 (&qreg)[18],
-                                        float* sx_mine, int lane) {
+                                        float* sx_mine, int lane, Issue&& issue) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     auto kchunk = [&](int row_hi, int t) -> f32x4 {
         const int tg = 18 * HALF + t;
@@ -184,6 +185,12 @@ __device__ __forceinline__ void qk_slot(const char* Kb, const TileOffsets& to, c
             s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(c0[u], qreg[t][u], s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(c1[u], qreg[t][u], s1, 0, 0, 0);
         }
+        // The next tile's loads go out here, behind a queue of MFMAs: issuing them
+        // (9 address computations and global_load_lds per wave) right after the
+        // barrier would delay the first MFMA by a few hundred cycles.  Measured
+        // on the 8-batch-row, 32768-prefix workload: after step 2 of 18 beats steps
+        // 1, 3 and 5 and a three-way split.
+        if (t == 2) issue();
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -318,14 +325,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();                                  // tile `it` is in LDS
         const bool more = it + 1 < ntiles;
-        if (more) {
-            if (!KV_BF16)
-                issue_tile_f32(sm.kv[(it + 1) & 1], a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, wave, lane);
-            else
-                load_tile_bf16(stage, a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, tid);
-        }
+        auto issue = [&]() {
+            if (more) {
+                if (!KV_BF16)
+                    issue_tile_f32(sm.kv[(it + 1) & 1], a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, wave, lane);
+                else
+                    load_tile_bf16(stage, a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, tid);
+            }
+        };
         const char* Kb = reinterpret_cast<const char*>(sm.kv[it & 1]);
-        qk_slot<HALF>(Kb, to, qreg, sx_mine, lane);
+        qk_slot<HALF>(Kb, to, qreg, sx_mine, lane, issue);
         __syncthreads();                                  // partner's partial scores are in LDS
         sm_pv_slot<HALF>(oacc, sx_mine, sx_partner, Kb, to, m_run, l_lane, mrow, g, n, lane, kv_lo + it * kTile, P,
                          kv_hi);
