@@ -131,7 +131,7 @@ __device__ __forceinline__ void store_tile_bf16(f32x4* buf, const Bf16Stage& st,
 
 struct Smem {
     f32x4 kv[2][kTileChunks];        // 2 x 72 KiB, double-buffered cache tile
-    float sx[kWaves][8][64];         // 16 KiB, partial scores swapped inside a wave pair
+    f32x4 sx[kWaves][2][64];         // 16 KiB, partial scores swapped inside a wave pair
 };
 
 // Per-lane byte offsets inside a tile buffer, derived from the swizzle (chunk c
@@ -165,7 +165,7 @@ __device__ __forceinline__ f32x4 lds16(const char* base, uint32_t off) {
 // area; issue() starts the next tile's loads part-way through.
 template <int HALF, class Issue>
 __device__ __forceinline__ void qk_slot(const char* Kb, const TileOffsets& to, const f32x4 (&qreg)[18],
-                                        float* sx_mine, int lane, Issue&& issue) {
+                                        f32x4* sx_mine, int lane, Issue&& issue) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     auto kchunk = [&](int row_hi, int t) -> f32x4 {
         const int tg = 18 * HALF + t;
@@ -192,25 +192,26 @@ __device__ __forceinline__ void qk_slot(const char* Kb, const TileOffsets& to, c
         // 1, 3 and 5 and a three-way split.
         if (t == 2) issue();
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        sx_mine[e * 64 + lane] = s0[e];
-        sx_mine[(4 + e) * 64 + lane] = s1[e];
-    }
+    sx_mine[lane] = s0;
+    sx_mine[64 + lane] = s1;
 }
 
 // Full scores of the tile starting at cache position t0 (own partial and the
 // partner's, both from LDS), online softmax, then O += P V over this wave's 256 dims.
 template <int HALF>
-__device__ __forceinline__ void sm_pv_slot(f32x4 (&oacc)[16], const float* sx_mine, const float* sx_partner,
+__device__ __forceinline__ void sm_pv_slot(f32x4 (&oacc)[16], const f32x4* sx_mine, const f32x4* sx_partner,
                                            const char* Kb, const TileOffsets& to, float& m_run, float& l_lane,
                                            const uint32_t* mrow, int g, int n, int lane, int t0, int P,
                                            int kv_hi) {
     float sv[8];
+    {
+        const f32x4 a0 = sx_mine[lane] + sx_partner[lane];
+        const f32x4 a1 = sx_mine[64 + lane] + sx_partner[64 + lane];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        sv[e] = sx_mine[e * 64 + lane] + sx_partner[e * 64 + lane];
-        sv[4 + e] = sx_mine[(4 + e) * 64 + lane] + sx_partner[(4 + e) * 64 + lane];
+        for (int e = 0; e < 4; ++e) {
+            sv[e] = a0[e];
+            sv[4 + e] = a1[e];
+        }
     }
     const bool full = (t0 + kTile <= P) && (t0 + kTile <= kv_hi);
     float tmax = -INFINITY;
@@ -319,8 +320,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
     if (KV_BF16) store_tile_bf16(sm.kv[0], stage, tid);
 
     const TileOffsets to = tile_offsets(g, n);
-    float* sx_mine = &sm.sx[wave][0][0];
-    const float* sx_partner = &sm.sx[wave ^ 1][0][0];
+    f32x4* sx_mine = &sm.sx[wave][0][0];
+    const f32x4* sx_partner = &sm.sx[wave ^ 1][0][0];
     for (int it = 0; it < ntiles; ++it) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();                                  // tile `it` is in LDS
