@@ -75,16 +75,6 @@ __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v 
 // Wave-level butterflies (wave64).
 __device__ __forceinline__ float wave_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
-// Is tree column a (0 <= a < Q) set in a row's mask words?  w[] holds kMaxW words;
-// the index is dynamic, so select with a compare chain instead of scratch.
-__device__ __forceinline__ bool mask_bit(const uint32_t (&w)[kMaxW], int a) {
-    const int wi = a >> 5;
-    uint32_t word = w[0];
-#pragma unroll
-    for (int k = 1; k < kMaxW; ++k) word = (wi == k) ? w[k] : word;
-    return (word >> (a & 31)) & 1u;
-}
-
 #endif
 
 }  // namespace ddtv
