@@ -322,6 +322,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
     const TileOffsets to = tile_offsets(g, n);
     f32x4* sx_mine = &sm.sx[wave][0][0];
     const f32x4* sx_partner = &sm.sx[wave ^ 1][0][0];
+    // A pair whose 16 rows all lie beyond the batch row's H*Q query rows (small
+    // trees, few heads) only loads tiles and meets the barriers: its matrix work
+    // would be discarded, and skipping it frees the SIMDs for the pairs with rows.
+    const bool pair_active = rt * kRows + pair * 16 < a.R;
     for (int it = 0; it < ntiles; ++it) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();                                  // tile `it` is in LDS
@@ -335,10 +339,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
             }
         };
         const char* Kb = reinterpret_cast<const char*>(sm.kv[it & 1]);
-        qk_slot<HALF>(Kb, to, qreg, sx_mine, lane, issue);
+        if (pair_active)
+            qk_slot<HALF>(Kb, to, qreg, sx_mine, lane, issue);
+        else
+            issue();
         __syncthreads();                                  // partner's partial scores are in LDS
-        sm_pv_slot<HALF>(oacc, sx_mine, sx_partner, Kb, to, m_run, l_lane, mrow, g, n, lane, kv_lo + it * kTile, P,
-                         kv_hi);
+        if (pair_active)
+            sm_pv_slot<HALF>(oacc, sx_mine, sx_partner, Kb, to, m_run, l_lane, mrow, g, n, lane, kv_lo + it * kTile,
+                             P, kv_hi);
         if (KV_BF16 && more) store_tile_bf16(sm.kv[(it + 1) & 1], stage, tid);
     }
 
