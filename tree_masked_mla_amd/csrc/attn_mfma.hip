@@ -323,9 +323,25 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
     f32x4* sx_mine = &sm.sx[wave][0][0];
     const f32x4* sx_partner = &sm.sx[wave ^ 1][0][0];
     // A pair whose 16 rows all lie beyond the batch row's H*Q query rows (small
-    // trees, few heads) only loads tiles and meets the barriers: its matrix work
-    // would be discarded, and skipping it frees the SIMDs for the pairs with rows.
-    const bool pair_active = rt * kRows + pair * 16 < a.R;
+    // trees, few heads) only loads its share of the tiles and meets the barriers:
+    // its matrix work would be discarded, and skipping it frees the SIMDs for the
+    // pairs with rows.  (A separate loop, so the main loop's code is unchanged.)
+    if (rt * kRows + pair * 16 >= a.R) {
+        for (int it = 0; it < ntiles; ++it) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            const bool more = it + 1 < ntiles;
+            if (more) {
+                if (!KV_BF16)
+                    issue_tile_f32(sm.kv[(it + 1) & 1], a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, wave, lane);
+                else
+                    load_tile_bf16(stage, a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, tid);
+            }
+            __syncthreads();
+            if (KV_BF16 && more) store_tile_bf16(sm.kv[(it + 1) & 1], stage, tid);
+        }
+        return;   // no rows to write
+    }
     for (int it = 0; it < ntiles; ++it) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();                                  // tile `it` is in LDS
@@ -339,14 +355,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
             }
         };
         const char* Kb = reinterpret_cast<const char*>(sm.kv[it & 1]);
-        if (pair_active)
-            qk_slot<HALF>(Kb, to, qreg, sx_mine, lane, issue);
-        else
-            issue();
+        qk_slot<HALF>(Kb, to, qreg, sx_mine, lane, issue);
         __syncthreads();                                  // partner's partial scores are in LDS
-        if (pair_active)
-            sm_pv_slot<HALF>(oacc, sx_mine, sx_partner, Kb, to, m_run, l_lane, mrow, g, n, lane, kv_lo + it * kTile,
-                             P, kv_hi);
+        sm_pv_slot<HALF>(oacc, sx_mine, sx_partner, Kb, to, m_run, l_lane, mrow, g, n, lane, kv_lo + it * kTile, P,
+                         kv_hi);
         if (KV_BF16 && more) store_tile_bf16(sm.kv[(it + 1) & 1], stage, tid);
     }
 

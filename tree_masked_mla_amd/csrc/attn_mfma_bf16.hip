@@ -388,9 +388,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
 
     f32x4* sx_mine = &sm.sx[wave][0][0];
     const f32x4* sx_partner = &sm.sx[wave ^ 1][0][0];
-    // A pair whose 16 rows all lie beyond the batch row's H*Q query rows only loads
-    // tiles and meets the barriers (its matrix work would be discarded).
-    const bool pair_active = rt * kRows + pair * 16 < a.R;
     auto buf = [&](int t) { return ring0 + (uint32_t)(t & (kRing - 1)) * kBufBytes; };
     // Tile m goes into the buffer of tile m-4, whose last reader (group 1's P.V of
     // tile m-4) ran in slot 2m-5.  Each wave issues its share of a tile during its
@@ -414,36 +411,32 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
     // of the last tile.  Tiles 0 and 1 are issued before the loop.
     if (grp == 0) {
         for (int t = 0; t < ntiles; ++t) {
-            if (pair_active) {
-                if (t == 0)
-                    mfma_slot<HALF, false, true>(oacc, sa, pa, qreg, toff, koff, 0, buf(t), sx_mine, lane);
-                else
-                    mfma_slot<HALF, true, true>(oacc, sa, pa, qreg, toff, koff, buf(t - 1), buf(t), sx_mine, lane);
-            }
+            if (t == 0)
+                mfma_slot<HALF, false, true>(oacc, sa, pa, qreg, toff, koff, 0, buf(t), sx_mine, lane);
+            else
+                mfma_slot<HALF, true, true>(oacc, sa, pa, qreg, toff, koff, buf(t - 1), buf(t), sx_mine, lane);
             slot_barrier();                                                 // slot 2t
             issue(t + 2);
-            if (pair_active) softmax_slot(oacc, sa, pa, m_run, l_lane, sx_partner, lane, kv_lo + t * kTile, P, kv_hi, mrow);
+            softmax_slot(oacc, sa, pa, m_run, l_lane, sx_partner, lane, kv_lo + t * kTile, P, kv_hi, mrow);
             end_odd_slot(t + 1);                                            // slot 2t+1
         }
-        if (pair_active) mfma_slot<HALF, true, false>(oacc, sa, pa, qreg, toff, koff, buf(ntiles - 1), 0, sx_mine, lane);
+        mfma_slot<HALF, true, false>(oacc, sa, pa, qreg, toff, koff, buf(ntiles - 1), 0, sx_mine, lane);
         slot_barrier();                                                     // slot 2n
         slot_barrier();                                                     // slot 2n+1 (idle)
     } else {
         issue(2);
         slot_barrier();                                                     // slot 0 (idle)
         for (int t = 0; t < ntiles; ++t) {
-            if (pair_active) {
-                if (t == 0)
-                    mfma_slot<HALF, false, true>(oacc, sa, pa, qreg, toff, koff, 0, buf(t), sx_mine, lane);
-                else
-                    mfma_slot<HALF, true, true>(oacc, sa, pa, qreg, toff, koff, buf(t - 1), buf(t), sx_mine, lane);
-            }
+            if (t == 0)
+                mfma_slot<HALF, false, true>(oacc, sa, pa, qreg, toff, koff, 0, buf(t), sx_mine, lane);
+            else
+                mfma_slot<HALF, true, true>(oacc, sa, pa, qreg, toff, koff, buf(t - 1), buf(t), sx_mine, lane);
             end_odd_slot(t + 1);                                            // slot 2t+1
             issue(t + 3);
-            if (pair_active) softmax_slot(oacc, sa, pa, m_run, l_lane, sx_partner, lane, kv_lo + t * kTile, P, kv_hi, mrow);
+            softmax_slot(oacc, sa, pa, m_run, l_lane, sx_partner, lane, kv_lo + t * kTile, P, kv_hi, mrow);
             slot_barrier();                                                 // slot 2t+2
         }
-        if (pair_active) mfma_slot<HALF, true, false>(oacc, sa, pa, qreg, toff, koff, buf(ntiles - 1), 0, sx_mine, lane);
+        mfma_slot<HALF, true, false>(oacc, sa, pa, qreg, toff, koff, buf(ntiles - 1), 0, sx_mine, lane);
         slot_barrier();                                                     // slot 2n+1
     }
 
