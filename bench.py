@@ -151,6 +151,7 @@ def main():
     ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA (cache precision), 3 fp32 MFMA")
     ap.add_argument("--split-len", type=int, default=0)
+    ap.add_argument("--wg-order", type=int, default=0, help="0 auto, 1 XCD-local, 2 spread")
     ap.add_argument("--q-len", type=int, default=0,
                     help="override the workload's tree size (probe runs, e.g. q_len 1 = decode); "
                          "not the benchmarked configuration")
@@ -192,9 +193,9 @@ def main():
                           "launches": args.copy_calibration}))
         return
 
-    r = DeviceRun(w, device=dev, path=args.path, split_len=args.split_len, want_lse=True)
-    rc, path, split_len, n_split, wgs = r.plan()
-    log(f"plan: path={path} split_len={split_len} n_split={n_split} workgroups={wgs}")
+    r = DeviceRun(w, device=dev, path=args.path, split_len=args.split_len, want_lse=True, wg_order=args.wg_order)
+    rc, path, split_len, n_split, wgs, wg_order = r.plan()
+    log(f"plan: path={path} split_len={split_len} n_split={n_split} workgroups={wgs} wg_order={wg_order}")
     hip = Hip()
     stream = torch.cuda.current_stream(dev).cuda_stream
     K = args.steps
@@ -208,7 +209,7 @@ def main():
     t_host0 = time.perf_counter()
     hip.record(ev_step0, stream)
     for k in range(K):
-        opts = dd.make_opts(args.path, args.split_len, ev_attn[k][0], ev_attn[k][1])
+        opts = dd.make_opts(args.path, args.split_len, ev_attn[k][0], ev_attn[k][1], args.wg_order)
         r.step(stream, opts)
     hip.record(ev_step1, stream)
     torch.cuda.synchronize()
@@ -247,7 +248,8 @@ def main():
         "config": {"workload": f"{args.config}: {desc}", "B": w.B, "H": w.H,
                    "q_len": w.Q, "prefix": "ragged" if args.config == "c5" else int(w.prefix[0]),
                    "total_kv_rows": w.total_kv, "scale": w.scale, "path": path, "split_len": split_len,
-                   "n_split": n_split, "workgroups": wgs},
+                   "n_split": n_split, "workgroups": wgs,
+                   "wg_order": {1: "xcd-local", 2: "spread"}.get(wg_order, wg_order)},
         "hbm_gbps": round(hbm_gbps, 2),
         "hbm_pct_of_peak": round(100.0 * hbm_gbps / HBM_PEAK_GBPS, 3),
         "attn_kernel_us": round(attn_avg_ms * 1e3, 2),

@@ -147,12 +147,27 @@ typedef enum {
                                fp32): slower on bf16 caches, fp32-accurate */
 } ddtv_path;
 
+/* Order in which the main kernel's workgroups take their work items (batch row,
+ * KV split, 64-row query tile).  MI355X deals workgroup i to XCD i % 8, and each
+ * XCD has its own L2.  The order changes only which workgroup computes which
+ * item: outputs are bit-identical under every order. */
+typedef enum {
+    DDTV_ORDER_AUTO = 0,       /* the planner picks the one with the shorter simulated schedule */
+    DDTV_ORDER_XCD_LOCAL = 1,  /* consecutive work items on one XCD: the query tiles that read a
+                                  cache tile share that XCD's L2; but each XCD then owns whole
+                                  batch rows, which unbalances the XCDs when rows differ in length */
+    DDTV_ORDER_SPREAD = 2      /* work item i on workgroup i: a batch row's query tiles go round
+                                  all XCDs, which balances ragged batches; each XCD then reads
+                                  every cache tile its query tiles need */
+} ddtv_wg_order;
+
 /* Optional controls for ddtv_verify_attn_ex (zero-initialise for defaults). */
 typedef struct {
     int32_t path;          /* ddtv_path */
     int32_t split_len;     /* KV positions per split; 0 = automatic; else a multiple of 32 */
     hipEvent_t attn_begin; /* if non-NULL: recorded on `stream` right before the main kernel */
     hipEvent_t attn_end;   /* if non-NULL: recorded on `stream` right after it (before the merge) */
+    int32_t wg_order;      /* ddtv_wg_order */
 } ddtv_opts;
 
 /* Workspace bytes ddtv_verify_attn(_ex) needs for this visibility, head count and
@@ -200,10 +215,11 @@ ddtv_status ddtv_verify_attn_ex(const float *q_abs, const float *q_rope, const v
 
 /* Describes the plan ddtv_verify_attn_ex would run (HOST out params, may be NULL):
  * path taken, KV positions per split, maximum splits per batch row, workgroups
- * of the main kernel.  Returns DDTV_EINVAL/DDTV_EUNSUPPORTED like the call would. */
+ * of the main kernel, workgroup order (DDTV_ORDER_XCD_LOCAL or DDTV_ORDER_SPREAD).
+ * Returns DDTV_EINVAL/DDTV_EUNSUPPORTED like the call would. */
 ddtv_status ddtv_plan_info(const ddtv_vis *vis, int32_t H, ddtv_dtype kv_dtype,
                            const ddtv_opts *opts, int32_t *path, int32_t *split_len,
-                           int32_t *n_split, int64_t *workgroups);
+                           int32_t *n_split, int64_t *workgroups, int32_t *wg_order);
 
 /* Static description of a status code. */
 const char *ddtv_status_string(ddtv_status s);

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert dd.ddtv_version() == 200
+    assert dd.ddtv_version() == 300
     for code in range(6):
         assert dd.ddtv_status_string(code)
     assert dd.ddtv_status_string(2).startswith("malformed tree")
@@ -116,6 +116,7 @@ def test_verify_host_errors(lib):
     assert verify_call(lib, vis, opts=dd.make_opts(path=4)) == U
     assert verify_call(lib, vis, opts=dd.make_opts(split_len=100)) == E   # not a multiple of 32
     assert verify_call(lib, vis, opts=dd.make_opts(split_len=-64)) == E
+    assert verify_call(lib, vis, opts=dd.make_opts(wg_order=3)) == U
     bad = fake_vis()
     bad.vis.W = 2
     assert verify_call(lib, bad) == E
@@ -141,14 +142,14 @@ def test_plan_rules(lib):
                        (1, 16, dd.DDTV_PATH_MFMA), (16, 1, dd.DDTV_PATH_MFMA), (9, 8, dd.DDTV_PATH_MFMA),
                        (128, 16, dd.DDTV_PATH_MFMA)]:
         vis = fake_vis(B=1, Q=Q, prefix=(100,))
-        rc, path, L, ns, wg = dd.ddtv_plan_info(vis, H, 0)
+        rc, path, L, ns, wg, order = dd.ddtv_plan_info(vis, H, 0)
         assert rc == 0 and path == want, (Q, H, path)
     vis = fake_vis(B=1, Q=9, prefix=(100,))
     assert dd.ddtv_plan_info(vis, 8, 0, dd.make_opts(path=dd.DDTV_PATH_MFMA))[1] == dd.DDTV_PATH_MFMA
     # a forced split length gives ceil(max_kv / L) splits and a matching workspace
     vis = fake_vis(B=2, Q=64, prefix=(1000, 5000))
     opts = dd.make_opts(split_len=1024)
-    rc, path, L, ns, wg = dd.ddtv_plan_info(vis, 16, 0, opts)
+    rc, path, L, ns, wg, order = dd.ddtv_plan_info(vis, 16, 0, opts)
     assert (L, ns) == (1024, (5064 + 1023) // 1024)
     R = 64 * 16
     assert wg == 2 * ns * ((R + 63) // 64)
@@ -163,12 +164,33 @@ def test_plan_rules(lib):
 def test_auto_plan_shapes(lib):
     """The automatic planner fills the device with small grids and keeps big ones whole."""
     vis = fake_vis(B=1, Q=64, prefix=(4096,))          # 16 row tiles: must split
-    rc, path, L, ns, wg = dd.ddtv_plan_info(vis, 16, 0)
+    rc, path, L, ns, wg, order = dd.ddtv_plan_info(vis, 16, 0)
     assert rc == 0 and ns > 1 and wg >= 128
     vis = fake_vis(B=8, Q=128, prefix=(32768,) * 8)    # 256 row tiles of equal work
-    rc, path, L, ns, wg = dd.ddtv_plan_info(vis, 16, 0)
+    rc, path, L, ns, wg, order = dd.ddtv_plan_info(vis, 16, 0)
     assert rc == 0 and wg >= 256
     assert L % 64 == 0
+
+
+def test_workgroup_order_rules(lib):
+    """Equal-length batch rows keep the XCD-local order (each XCD's L2 serves the
+    query tiles that share a cache tile); when one row is far longer than the
+    rest, XCD-local would leave that row's XCD with most of the work, so the
+    planner spreads each row's query tiles over all XCDs.  Forced orders are
+    honoured and change nothing else in the plan."""
+    vis = fake_vis(B=8, Q=128, prefix=(32768,) * 8)
+    rc, path, L, ns, wg, order = dd.ddtv_plan_info(vis, 16, 0)
+    assert rc == 0 and order == dd.DDTV_ORDER_XCD_LOCAL
+    ragged = fake_vis(B=8, Q=64, prefix=(131072,) + (1024,) * 7)
+    for dtype in (0, 1):
+        rc, path, L, ns, wg, order = dd.ddtv_plan_info(ragged, 64, dtype)
+        assert rc == 0 and order == dd.DDTV_ORDER_SPREAD, dtype
+    for want in (dd.DDTV_ORDER_XCD_LOCAL, dd.DDTV_ORDER_SPREAD):
+        opts = dd.make_opts(split_len=4096, wg_order=want)
+        rc, path, L, ns, wg, order = dd.ddtv_plan_info(ragged, 64, 1, opts)
+        assert (rc, L, order) == (0, 4096, want)
+        assert ns == (131072 + 64 + 4095) // 4096 and wg == 8 * ns * 64
+    assert dd.ddtv_plan_info(ragged, 64, 1, dd.make_opts(wg_order=7))[0] == dd.DDTV_EUNSUPPORTED
 
 
 def test_oracle_shares_error_contract(lib):

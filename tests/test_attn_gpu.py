@@ -18,19 +18,20 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 
-def run(w, path=0, split_len=0, bits_override=None, parent=None):
+def run(w, path=0, split_len=0, bits_override=None, parent=None, wg_order=0):
     from tree_masked_mla_amd.runner import DeviceRun
-    r = DeviceRun(w, path=path, split_len=split_len, bits_override=bits_override, parent=parent)
+    r = DeviceRun(w, path=path, split_len=split_len, bits_override=bits_override, parent=parent,
+                  wg_order=wg_order)
     r.step()
     out, lse = r.results()
     return r, out, lse
 
 
-def check_full(w, path=0, split_len=0, what=None):
+def check_full(w, path=0, split_len=0, what=None, wg_order=0):
     what = what or w.name
-    say(f"attn {what} path={path} split={split_len}")
+    say(f"attn {what} path={path} split={split_len} order={wg_order}")
     bits, _, _ = oracle.build_visibility(w.parent)
-    r, out, lse = run(w, path, split_len)
+    r, out, lse = run(w, path, split_len, wg_order=wg_order)
     assert np.array_equal(r.bits(), bits)
     ref, rlse = oracle_rows(w, bits)
     e = assert_close(out, ref, w.kv_dtype, what)
@@ -126,6 +127,23 @@ def test_path_invariance():
     assert run(w)[0].plan()[1] == 2      # auto: 128 query rows per batch row -> MFMA
     w15 = wl.make_workload("q15", 3015, B=1, H=1, Q=15, prefix=[40], tree="uniform")
     assert run(w15)[0].plan()[1] == 1    # and VALU below 16 rows
+
+
+@pytest.mark.parametrize("path,kv_dtype", [(1, 0), (2, 0), (2, 1)])
+def test_workgroup_order_changes_nothing(path, kv_dtype):
+    """The XCD-local and spread work-item orders only change which workgroup
+    computes which (batch row, split, query tile): on ragged rows with many
+    splits and several query tiles, outputs and lse are bit-identical under both,
+    and match the oracle."""
+    w = wl.make_workload("ragged", 4100 + 10 * path + kv_dtype, B=5, H=16, Q=24,
+                         prefix=[700, 40, 1333, 0, 260], tree="uniform", kv_dtype=kv_dtype)
+    res = []
+    for order in (1, 2):
+        r, out, lse = check_full(w, path=path, split_len=128, what=f"order {order}", wg_order=order)
+        assert r.plan()[5] == order and r.plan()[3] > 1
+        res.append((out, lse))
+    assert np.array_equal(res[0][0], res[1][0])
+    assert np.array_equal(res[0][1], res[1][1])
 
 
 # ----------------------------------------------------------------------------- edge cases

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libddtv.so")
 DDTV_OK, DDTV_EINVAL, DDTV_ETREE, DDTV_EUNSUPPORTED, DDTV_EWORKSPACE, DDTV_EDEVICE = range(6)
 DDTV_F32, DDTV_BF16 = 0, 1
 DDTV_PATH_AUTO, DDTV_PATH_VALU, DDTV_PATH_MFMA, DDTV_PATH_MFMA_F32 = 0, 1, 2, 3
+DDTV_ORDER_AUTO, DDTV_ORDER_XCD_LOCAL, DDTV_ORDER_SPREAD = 0, 1, 2
 D_LATENT, D_ROPE, MAX_Q = 512, 64, 256
 
 EXPORTED = (
@@ -49,7 +50,7 @@ class ddtv_vis(ctypes.Structure):
 
 class ddtv_opts(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("split_len", ctypes.c_int32),
-                ("attn_begin", ctypes.c_void_p), ("attn_end", ctypes.c_void_p)]
+                ("attn_begin", ctypes.c_void_p), ("attn_end", ctypes.c_void_p), ("wg_order", ctypes.c_int32)]
 
 
 _lib = None
@@ -80,7 +81,7 @@ def load(path: str = LIB_PATH):
     lib.ddtv_verify_attn_ex.argtypes = [P, P, P, P, ctypes.c_int, i32, VP, ctypes.c_float, P, P, P, sz, P, OP]
     lib.ddtv_verify_attn_ex.restype = ctypes.c_int
     lib.ddtv_plan_info.argtypes = [VP, i32, ctypes.c_int, OP, ctypes.POINTER(i32), ctypes.POINTER(i32),
-                                   ctypes.POINTER(i32), ctypes.POINTER(i64)]
+                                   ctypes.POINTER(i32), ctypes.POINTER(i64), ctypes.POINTER(i32)]
     lib.ddtv_plan_info.restype = ctypes.c_int
     lib.ddtv_status_string.argtypes = [ctypes.c_int]
     lib.ddtv_status_string.restype = ctypes.c_char_p
@@ -119,8 +120,9 @@ def _event(ev) -> int | None:
     return ev.cuda_event
 
 
-def make_opts(path: int = DDTV_PATH_AUTO, split_len: int = 0, attn_begin=None, attn_end=None) -> ddtv_opts:
-    return ddtv_opts(path, split_len, _event(attn_begin), _event(attn_end))
+def make_opts(path: int = DDTV_PATH_AUTO, split_len: int = 0, attn_begin=None, attn_end=None,
+              wg_order: int = DDTV_ORDER_AUTO) -> ddtv_opts:
+    return ddtv_opts(path, split_len, _event(attn_begin), _event(attn_end), wg_order)
 
 
 class Visibility:
@@ -175,13 +177,14 @@ def ddtv_workspace_bytes(vis: Visibility, H: int, kv_dtype: int, opts: ddtv_opts
 
 
 def ddtv_plan_info(vis: Visibility, H: int, kv_dtype: int, opts: ddtv_opts | None = None):
-    """Returns (status, path, split_len, n_split, workgroups)."""
-    p, L, ns = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    """Returns (status, path, split_len, n_split, workgroups, wg_order)."""
+    p, L, ns, order = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     wg = ctypes.c_int64()
     rc = load().ddtv_plan_info(ctypes.byref(vis.vis), H, kv_dtype,
                                ctypes.byref(opts) if opts is not None else None,
-                               ctypes.byref(p), ctypes.byref(L), ctypes.byref(ns), ctypes.byref(wg))
-    return rc, p.value, L.value, ns.value, wg.value
+                               ctypes.byref(p), ctypes.byref(L), ctypes.byref(ns), ctypes.byref(wg),
+                               ctypes.byref(order))
+    return rc, p.value, L.value, ns.value, wg.value, order.value
 
 
 def ddtv_verify_attn(q_abs, q_rope, ckv, k_rope, kv_dtype: int, H: int, vis: Visibility, scale: float, out,

@@ -17,7 +17,7 @@ using namespace ddtv;
 
 namespace {
 
-constexpr int32_t kVersion = 200;   // 0.2.0: automatic path by query rows per batch row
+constexpr int32_t kVersion = 300;   // 0.3.0: workgroup order (XCD-local or spread) in the plan
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -64,32 +64,49 @@ struct Plan {
     int n_rt = 0;
     int split_len = 0;
     int n_split = 1;
+    int order = DDTV_ORDER_XCD_LOCAL;
     int64_t grid = 0;
     size_t ws_part_o = 0, ws_part_ml = 0, ws_bytes = 0;
 };
 
-// Estimated makespan (in tile-times) of a grid of workgroups dealt in order onto
-// `cus` compute units, one workgroup per CU at a time (both kernels use most of
-// a CU's LDS), plus the cost of the merge pass.
+// Estimated makespan (in tile-times) of the main kernel's grid plus the merge
+// pass.  The grid holds B x n_split x n_rt work items (batch row slowest, query
+// tile fastest; items past a short row's last split exit at once).  The
+// dispatcher deals workgroup i to XCD i % 8, and each XCD starts its workgroups
+// in order on whichever of its CUs frees first, one workgroup per CU at a time
+// (every attention kernel uses most of a CU's LDS).  Workgroup i runs work item
+// i (spread) or xcd_remap(i) (XCD-local).
 double estimate(const std::vector<int>& kv, int n_rt, int L, int cus, double setup_tiles,
-                double merge_tiles_per_partial_row_split, int64_t R) {
-    std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
-    for (int i = 0; i < cus; ++i) free_at.push(0.0);
+                double merge_tiles_per_partial_row_split, int64_t R, bool spread) {
+    typedef std::priority_queue<double, std::vector<double>, std::greater<double>> MinHeap;
+    const int per_xcd = std::max(1, cus / kXcds);
+    std::vector<MinHeap> free_at(kXcds);
+    for (auto& h : free_at)
+        for (int i = 0; i < per_xcd; ++i) h.push(0.0);
+    int n_split = 1;
+    for (int k : kv) n_split = std::max(n_split, (k + L - 1) / L);
+    const int64_t G = (int64_t)kv.size() * n_split * n_rt;
     double makespan = 0.0, merge = 0.0;
-    for (size_t b = 0; b < kv.size(); ++b) {
-        const int nb = (kv[b] + L - 1) / L;
-        for (int s = 0; s < nb; ++s) {
-            const int len = std::min(L, kv[b] - s * L);
-            const double cost = setup_tiles + (len + kTile - 1) / kTile;
-            for (int r = 0; r < n_rt; ++r) {
-                double t = free_at.top();
-                free_at.pop();
-                t += cost;
-                makespan = std::max(makespan, t);
-                free_at.push(t);
-            }
-        }
+    for (int k : kv) {
+        const int nb = (k + L - 1) / L;
         if (nb > 1) merge += merge_tiles_per_partial_row_split * (double)nb * (double)R;
+    }
+    if (G > ((int64_t)1 << 22)) {   // too many to simulate: thousands per CU even out
+        double work = 0.0;
+        for (int k : kv) work += (double)n_rt * ((k + kTile - 1) / kTile + setup_tiles * ((k + L - 1) / L));
+        return work / cus + merge;
+    }
+    for (int64_t i = 0; i < G; ++i) {
+        const int64_t w = spread ? i : xcd_remap(i, G);
+        const int b = (int)(w / ((int64_t)n_rt * n_split));
+        const int s = (int)((w / n_rt) % n_split);
+        const int len = std::min(L, kv[b] - s * L);
+        const double cost = len > 0 ? setup_tiles + (len + kTile - 1) / kTile : 0.02;
+        MinHeap& h = free_at[i % kXcds];
+        const double t = h.top() + cost;
+        h.pop();
+        h.push(t);
+        makespan = std::max(makespan, t);
     }
     return makespan + merge;
 }
@@ -102,7 +119,7 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
 // the last few plans are kept (the split search simulates a schedule and is too
 // slow to repeat per call).
 struct PlanKey {
-    int32_t B, Q, W, max_kv, H, dtype, path, split, cus;
+    int32_t B, Q, W, max_kv, H, dtype, path, split, order, cus;
     int64_t total_kv;
     uint64_t prefix_hash;
     bool operator==(const PlanKey& o) const { return memcmp(this, &o, sizeof *this) == 0; }
@@ -132,6 +149,7 @@ ddtv_status make_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const
     key.dtype = kv_dtype;
     key.path = opts ? opts->path : 0;
     key.split = opts ? opts->split_len : 0;
+    key.order = opts ? opts->wg_order : 0;
     key.cus = cu_count();
     key.prefix_hash = hash_prefix(vis);
     static std::mutex mu;
@@ -168,6 +186,9 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
         return DDTV_EUNSUPPORTED;
     const int split_req = opts ? opts->split_len : 0;
     if (split_req < 0 || (split_req % kSplitQuantum) != 0) return DDTV_EINVAL;
+    const int order_req = opts ? opts->wg_order : DDTV_ORDER_AUTO;
+    if (order_req != DDTV_ORDER_AUTO && order_req != DDTV_ORDER_XCD_LOCAL && order_req != DDTV_ORDER_SPREAD)
+        return DDTV_EUNSUPPORTED;
 
     // Auto: the matrix cores once a batch row's query rows fill a 16-row MFMA tile.
     // All heads share the latent cache, so the H * Q rows of a batch row contract
@@ -184,23 +205,39 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     const int max_kv = vis->max_kv;
     const int single = (int)round_up((size_t)max_kv, kSplitQuantum);
 
+    std::vector<int> kv(vis->B);
+    for (int b = 0; b < vis->B; ++b) kv[b] = vis->prefix_host ? vis->prefix_host[b] + vis->Q : max_kv;
+    const int cus = cu_count();
+    // Tile-time units: one 32-row cache tile through one workgroup.  A partial
+    // row costs 2 x 2 KiB of traffic in the merge (written, then read).
+    // tile_us: rough time of one tile through one workgroup (fp32 MFMA and bf16
+    // MFMA: 64 rows; VALU: 16 rows)
+    const bool mfma = p->path != DDTV_PATH_VALU;
+    const double setup = mfma ? 2.0 : 1.0;
+    const double tile_us = p->bf16_mma ? 0.9 : (mfma ? 7.3 : 1.0);
+    const double merge_per_row_split = (4096.0 / 4.0e12) * 1e6 / tile_us;   // ~4 TB/s effective
+    // Simulated makespan at split length L under the requested order, or under the
+    // better of the two.  The XCD-local order lets every query tile that reads a
+    // cache tile find it in its XCD's L2, so the spread order has to be clearly
+    // shorter to be chosen (it is when batch rows differ in length: XCD-local
+    // then gives each XCD whole rows).
+    auto cost_at = [&](int L, int* order) {
+        if (order_req != DDTV_ORDER_AUTO) {
+            *order = order_req;
+            return estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, order_req == DDTV_ORDER_SPREAD);
+        }
+        const double local = estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, false);
+        const double spread = estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, true);
+        *order = spread < local * 0.98 ? DDTV_ORDER_SPREAD : DDTV_ORDER_XCD_LOCAL;
+        return std::min(local, spread);
+    };
+
     if (split_req > 0) {
         p->split_len = split_req;
+        cost_at(split_req, &p->order);
     } else {
-        std::vector<int> kv(vis->B);
-        for (int b = 0; b < vis->B; ++b)
-            kv[b] = vis->prefix_host ? vis->prefix_host[b] + vis->Q : max_kv;
-        const int cus = cu_count();
-        // Tile-time units: one 32-row cache tile through one workgroup.  A partial
-        // row costs 2 x 2 KiB of traffic in the merge (written, then read).
-        // tile_us: rough time of one tile through one workgroup (fp32 MFMA and bf16
-        // MFMA: 64 rows; VALU: 16 rows)
-        const bool mfma = p->path != DDTV_PATH_VALU;
-        const double setup = mfma ? 2.0 : 1.0;
-        const double tile_us = p->bf16_mma ? 0.9 : (mfma ? 7.3 : 1.0);
-        const double merge_per_row_split = (4096.0 / 4.0e12) * 1e6 / tile_us;   // ~4 TB/s effective
         double best = 1e300;
-        int bestL = single;
+        int bestL = single, bestOrder = DDTV_ORDER_XCD_LOCAL;
         const int64_t wg_cap = (int64_t)cus * 64;
         // Candidates: the longest row cut into S equal tile-aligned pieces, S = 1, 2, ...
         // (stop once the grid is far beyond the device or pieces get short).
@@ -213,10 +250,12 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
             int64_t wgs = 0;
             for (int b = 0; b < vis->B; ++b) wgs += (int64_t)((kv[b] + L - 1) / L) * p->n_rt;
             if (wgs > wg_cap && S > 1) break;
-            const double e = estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R);
+            int order = DDTV_ORDER_XCD_LOCAL;
+            const double e = cost_at(L, &order);
             if (e < best * 0.98) {   // prefer fewer splits unless clearly better
                 best = e;
                 bestL = L;
+                bestOrder = order;
                 worse = 0;
             } else if (wgs > 2 * (int64_t)cus && ++worse >= 8) {
                 break;               // past a full device and no longer improving
@@ -224,6 +263,7 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
             if (S >= 4096) break;
         }
         p->split_len = bestL;
+        p->order = bestOrder;
     }
     p->n_split = (max_kv + p->split_len - 1) / p->split_len;
     p->grid = (int64_t)vis->B * p->n_rt * p->n_split;
@@ -335,7 +375,8 @@ size_t ddtv_workspace_bytes(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype)
 }
 
 ddtv_status ddtv_plan_info(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const ddtv_opts* opts,
-                           int32_t* path, int32_t* split_len, int32_t* n_split, int64_t* workgroups) {
+                           int32_t* path, int32_t* split_len, int32_t* n_split, int64_t* workgroups,
+                           int32_t* wg_order) {
     Plan p;
     ddtv_status st = make_plan(vis, H, kv_dtype, opts, &p);
     if (st) return st;
@@ -343,6 +384,7 @@ ddtv_status ddtv_plan_info(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, 
     if (split_len) *split_len = p.split_len;
     if (n_split) *n_split = p.n_split;
     if (workgroups) *workgroups = p.grid;
+    if (wg_order) *wg_order = p.order;
     return DDTV_OK;
 }
 
@@ -382,6 +424,7 @@ ddtv_status ddtv_verify_attn_ex(const float* q_abs, const float* q_rope, const v
     a.n_rt = p.n_rt;
     a.split_len = p.split_len;
     a.n_split = p.n_split;
+    a.spread = p.order == DDTV_ORDER_SPREAD;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 
     if (opts && opts->attn_begin && hipEventRecord(opts->attn_begin, stream) != hipSuccess) return DDTV_EDEVICE;

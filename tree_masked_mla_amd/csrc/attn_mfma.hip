@@ -403,7 +403,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
 template <int KV_BF16>
 __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs a) {
     __shared__ Smem sm;
-    const int64_t w = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t w = work_item(a);
     const int rt = (int)(w % a.n_rt);
     const int s = (int)((w / a.n_rt) % a.n_split);
     const int b = (int)(w / ((int64_t)a.n_rt * a.n_split));

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
     __shared__ float4 skv[kTile][kStride];    // 72.5 KiB: one cache tile
     __shared__ uint32_t smask[kRows][kMaxW];
 
-    const int64_t w = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t w = work_item(a);
     const int rt = (int)(w % a.n_rt);
     const int s = (int)((w / a.n_rt) % a.n_split);
     const int b = (int)(w / ((int64_t)a.n_rt * a.n_split));

@@ -35,6 +35,7 @@ struct AttnArgs {
     int n_rt;                // row tiles per batch row
     int split_len;           // KV positions per split (multiple of kSplitQuantum)
     int n_split;             // splits per batch row in the grid (max over rows)
+    int spread;              // 1: work item = workgroup id; 0: XCD-local order (xcd_remap)
     float scale_log2;        // scale * log2(e)
 };
 
@@ -56,17 +57,23 @@ hipError_t launch_merge(const AttnArgs& a, hipStream_t stream);
 
 constexpr int kValuRows = 16;   // query rows per VALU workgroup
 
+// Work item of workgroup i in the XCD-local order: consecutive work items land
+// on the same XCD (the dispatcher deals workgroup i to XCD i % 8).  Bijective for
+// any grid.  Also used by the host planner to simulate the dispatch.
+__host__ __device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t G) {
+    const int64_t q = G / kXcds, r = G % kXcds;
+    const int64_t x = i % kXcds, k = i / kXcds;
+    return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
+
 // ---------------------------------------------------------------------------
 // Device helpers
 // ---------------------------------------------------------------------------
 #if defined(__HIPCC__)
 
-// Spread workgroup ids so that consecutive work items land on the same XCD
-// (the dispatcher deals workgroup i to XCD i % 8).  Bijective for any grid.
-__device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t G) {
-    const int64_t q = G / kXcds, r = G % kXcds;
-    const int64_t x = i % kXcds, k = i / kXcds;
-    return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+// Work item of this workgroup under the planned order.
+__device__ __forceinline__ int64_t work_item(const AttnArgs& a) {
+    return a.spread ? (int64_t)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }

@@ -7,7 +7,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (DDTV_BF16, DDTV_PATH_AUTO, check, ddtv_build_visibility, ddtv_plan_info, ddtv_vis_bytes,
+from . import (DDTV_BF16, DDTV_ORDER_AUTO, DDTV_PATH_AUTO, check, ddtv_build_visibility, ddtv_plan_info, ddtv_vis_bytes,
                ddtv_verify_attn, ddtv_workspace_bytes, load, make_opts)
 
 
@@ -22,7 +22,8 @@ class DeviceRun:
     """One workload resident on one GPU, ready to run verify steps."""
 
     def __init__(self, w, device="cuda:0", path: int = DDTV_PATH_AUTO, split_len: int = 0,
-                 want_lse: bool = True, parent=None, bits_override: np.ndarray | None = None):
+                 want_lse: bool = True, parent=None, bits_override: np.ndarray | None = None,
+                 wg_order: int = DDTV_ORDER_AUTO):
         load()
         self.w = w
         self.device = torch.device(device)
@@ -39,7 +40,7 @@ class DeviceRun:
         self.out = torch.empty((w.B, w.Q, w.H, 512), dtype=torch.float32, device=self.device)
         self.lse = torch.empty((w.B, w.Q, w.H), dtype=torch.float32, device=self.device) if want_lse else None
         self.vis_buf = torch.empty(ddtv_vis_bytes(w.B, w.Q), dtype=torch.uint8, device=self.device)
-        self.opts = make_opts(path, split_len)
+        self.opts = make_opts(path, split_len, wg_order=wg_order)
         self.bits_override = bits_override
         self.vis = self.build_visibility()
         self.ws_bytes = ddtv_workspace_bytes(self.vis, w.H, w.kv_dtype, self.opts)
