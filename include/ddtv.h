@@ -87,6 +87,9 @@ typedef struct {
     uint32_t *bits;      /* DEVICE [B][Q][W] */
     ddtv_row *rows;      /* DEVICE [B] */
     int32_t *status;     /* DEVICE [B]: -1 if row b is a valid tree, else its lowest bad node */
+    int32_t *order;      /* DEVICE [B] or NULL: the batch rows by cache length, longest first
+                            (equal lengths: lower row first); a permutation of 0..B-1.  The
+                            attention kernels start long rows first under the spread order. */
     const int32_t *prefix_host; /* HOST [B] or NULL: BORROWED from the build call; when set it
                                    must stay valid until the last verify call that plans with
                                    this struct returns (used only to balance KV splits) */
@@ -110,7 +113,7 @@ size_t ddtv_vis_bytes(int32_t B, int32_t Q);
  *              so keep it alive while the struct is used for verify calls (or set
  *              vis->prefix_host to NULL afterwards).
  *   vis_buf    DEVICE buffer of at least ddtv_vis_bytes(B, Q) bytes, 256-byte
- *              aligned; bits, rows and status are carved out of it.
+ *              aligned; bits, rows, status and order are carved out of it.
  *   vis        HOST struct filled on return (pointers into vis_buf).
  * Malformed trees are detected ON THE DEVICE: the call still returns DDTV_OK and
  * the lowest malformed node of each row is written to vis->status; a malformed
@@ -157,8 +160,9 @@ typedef enum {
                                   cache tile share that XCD's L2; but each XCD then owns whole
                                   batch rows, which unbalances the XCDs when rows differ in length */
     DDTV_ORDER_SPREAD = 2      /* work item i on workgroup i: a batch row's query tiles go round
-                                  all XCDs, which balances ragged batches; each XCD then reads
-                                  every cache tile its query tiles need */
+                                  all XCDs, which balances ragged batches, and batch rows start
+                                  longest first (vis->order, when set); each XCD then reads every
+                                  cache tile its query tiles need */
 } ddtv_wg_order;
 
 /* Optional controls for ddtv_verify_attn_ex (zero-initialise for defaults). */

@@ -84,13 +84,14 @@ def test_build_visibility_host_errors(lib):
                                      None) == E
 
 
-def fake_vis(B=2, Q=9, prefix=(37, 37)):
+def fake_vis(B=2, Q=9, prefix=(37, 37), order=True):
     v = dd.ddtv_vis()
     v.B, v.Q, v.W = B, Q, (Q + 31) // 32
     pre = np.asarray(prefix, np.int32)
     v.max_kv = int(pre.max()) + Q
     v.total_kv = int((pre.astype(np.int64) + Q).sum())
     v.bits, v.rows, v.status = FAKE, FAKE + 4096, FAKE + 8192
+    v.order = FAKE + 12288 if order else None
     v.prefix_host = pre.ctypes.data
     return dd.Visibility(v, (pre,))
 
@@ -191,6 +192,11 @@ def test_workgroup_order_rules(lib):
         assert (rc, L, order) == (0, 4096, want)
         assert ns == (131072 + 64 + 4095) // 4096 and wg == 8 * ns * 64
     assert dd.ddtv_plan_info(ragged, 64, 1, dd.make_opts(wg_order=7))[0] == dd.DDTV_EUNSUPPORTED
+    # rows of random length (the long ones anywhere in the batch): with the row-order
+    # table the spread grid starts the longest rows first and needs no KV split
+    pre = tuple(int(x) for x in np.random.default_rng(5).integers(1024, 131073, 32))
+    rc, path, L, ns, wg, order = dd.ddtv_plan_info(fake_vis(B=32, Q=64, prefix=pre), 64, 1)
+    assert (rc, order, ns) == (0, dd.DDTV_ORDER_SPREAD, 1)
 
 
 def test_oracle_shares_error_contract(lib):

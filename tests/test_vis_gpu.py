@@ -36,6 +36,17 @@ def gpu_bits(parent, prefix):
     return bits, status, kv_off, pk[:, 0], pk[:, 1], vis, (buf, par_d)
 
 
+def gpu_order(vis, keep):
+    """The row-order table S1 wrote: batch rows by cache length, longest first."""
+    buf = keep[0]
+    off = vis.order - buf.data_ptr()
+    return buf[off: off + 4 * vis.B].cpu().numpy().view(np.int32).copy()
+
+
+def longest_first(prefix):
+    return np.argsort(-np.asarray(prefix, np.int64), kind="stable").astype(np.int32)
+
+
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
 def test_vis_configs_bit_exact(name):
     # trees and prefixes are the first draws of each workload's stream
@@ -43,9 +54,10 @@ def test_vis_configs_bit_exact(name):
     parent, prefix = wl.config_trees(name)
     ref, bad, rc = oracle.build_visibility(parent)
     assert rc == 0
-    bits, status, kv_off, pk, kvl, vis, _ = gpu_bits(parent, prefix)
+    bits, status, kv_off, pk, kvl, vis, keep = gpu_bits(parent, prefix)
     assert np.array_equal(bits, ref)
     assert (status == -1).all()
+    assert np.array_equal(gpu_order(vis, keep), longest_first(prefix))
     exp_off = np.concatenate([[0], np.cumsum(prefix.astype(np.int64) + parent.shape[1])[:-1]])
     assert np.array_equal(kv_off, exp_off)
     assert np.array_equal(pk, prefix) and np.array_equal(kvl, prefix + parent.shape[1])
@@ -73,9 +85,12 @@ def test_vis_large_trees_and_many_rows():
     parent = np.stack(trees)
     prefix = rng.integers(0, 5000, size=len(trees)).astype(np.int32)
     ref, _, _ = oracle.build_visibility(parent)
-    bits, status, kv_off, pk, kvl, vis, _ = gpu_bits(parent, prefix)
+    bits, status, kv_off, pk, kvl, vis, keep = gpu_bits(parent, prefix)
     assert np.array_equal(bits, ref)
     assert (status == -1).all()
+    order = gpu_order(vis, keep)                  # written chunk by chunk, over several launches
+    assert np.array_equal(order, longest_first(prefix))
+    assert np.array_equal(np.sort(order), np.arange(len(prefix)))
     assert np.array_equal(kv_off, np.concatenate([[0], np.cumsum(prefix.astype(np.int64) + Q)[:-1]]))
     for Qs in (31, 32, 33, 63, 64, 65, 100):
         par = np.stack([wl.uniform_tree(rng, Qs) for _ in range(3)])

@@ -45,7 +45,7 @@ class ddtv_vis(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Q", ctypes.c_int32), ("W", ctypes.c_int32),
                 ("max_kv", ctypes.c_int32), ("total_kv", ctypes.c_int64),
                 ("bits", ctypes.c_void_p), ("rows", ctypes.c_void_p), ("status", ctypes.c_void_p),
-                ("prefix_host", ctypes.c_void_p)]
+                ("order", ctypes.c_void_p), ("prefix_host", ctypes.c_void_p)]
 
 
 class ddtv_opts(ctypes.Structure):

@@ -23,7 +23,7 @@ inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct VisLayout {
-    size_t bits, rows, status, total;
+    size_t bits, rows, status, order, total;
 };
 
 VisLayout vis_layout(int32_t B, int32_t Q) {
@@ -32,8 +32,20 @@ VisLayout vis_layout(int32_t B, int32_t Q) {
     L.bits = 0;
     L.rows = round_up((size_t)B * Q * W * sizeof(uint32_t), 256);
     L.status = L.rows + round_up((size_t)B * sizeof(ddtv_row), 256);
-    L.total = L.status + round_up((size_t)B * sizeof(int32_t), 256);
+    L.order = L.status + round_up((size_t)B * sizeof(int32_t), 256);
+    L.total = L.order + round_up((size_t)B * sizeof(int32_t), 256);
     return L;
+}
+
+// Batch rows by cache length, longest first (equal lengths: lower row first).
+// Under the spread order the grid visits rows in this order, so the longest
+// rows start first and the short ones fill in at the end (longest-processing-
+// time-first list scheduling).
+std::vector<int> longest_first(const int32_t* prefix, int B) {
+    std::vector<int> perm(B);
+    for (int b = 0; b < B; ++b) perm[b] = b;
+    if (prefix) std::stable_sort(perm.begin(), perm.end(), [&](int x, int y) { return prefix[x] > prefix[y]; });
+    return perm;
 }
 
 int cu_count() {
@@ -53,7 +65,7 @@ ddtv_status check_vis(const ddtv_vis* vis) {
     if (!vis || !vis->bits || !vis->rows) return DDTV_EINVAL;
     if (vis->B < 1 || vis->Q < 1 || vis->Q > kMaxQ || vis->W != (vis->Q + 31) / 32) return DDTV_EINVAL;
     if (vis->max_kv < vis->Q || vis->total_kv < (int64_t)vis->B * vis->Q) return DDTV_EINVAL;
-    if (!aligned(vis->bits, 4) || !aligned(vis->rows, 8)) return DDTV_EINVAL;
+    if (!aligned(vis->bits, 4) || !aligned(vis->rows, 8) || !aligned(vis->order, 4)) return DDTV_EINVAL;
     return DDTV_OK;
 }
 
@@ -119,7 +131,7 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
 // the last few plans are kept (the split search simulates a schedule and is too
 // slow to repeat per call).
 struct PlanKey {
-    int32_t B, Q, W, max_kv, H, dtype, path, split, order, cus;
+    int32_t B, Q, W, max_kv, H, dtype, path, split, order, has_order, cus;
     int64_t total_kv;
     uint64_t prefix_hash;
     bool operator==(const PlanKey& o) const { return memcmp(this, &o, sizeof *this) == 0; }
@@ -150,6 +162,7 @@ ddtv_status make_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const
     key.path = opts ? opts->path : 0;
     key.split = opts ? opts->split_len : 0;
     key.order = opts ? opts->wg_order : 0;
+    key.has_order = vis->order != nullptr;
     key.cus = cu_count();
     key.prefix_hash = hash_prefix(vis);
     static std::mutex mu;
@@ -205,8 +218,15 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     const int max_kv = vis->max_kv;
     const int single = (int)round_up((size_t)max_kv, kSplitQuantum);
 
-    std::vector<int> kv(vis->B);
+    std::vector<int> kv(vis->B), kv_sorted(vis->B);
     for (int b = 0; b < vis->B; ++b) kv[b] = vis->prefix_host ? vis->prefix_host[b] + vis->Q : max_kv;
+    // the grid's batch-row order under the spread order (the row-order table, when present)
+    if (vis->order) {
+        const std::vector<int> perm = longest_first(vis->prefix_host, vis->B);
+        for (int b = 0; b < vis->B; ++b) kv_sorted[b] = kv[perm[b]];
+    } else {
+        kv_sorted = kv;
+    }
     const int cus = cu_count();
     // Tile-time units: one 32-row cache tile through one workgroup.  A partial
     // row costs 2 x 2 KiB of traffic in the merge (written, then read).
@@ -224,10 +244,12 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     auto cost_at = [&](int L, int* order) {
         if (order_req != DDTV_ORDER_AUTO) {
             *order = order_req;
-            return estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, order_req == DDTV_ORDER_SPREAD);
+            return order_req == DDTV_ORDER_SPREAD
+                       ? estimate(kv_sorted, p->n_rt, L, cus, setup, merge_per_row_split, R, true)
+                       : estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, false);
         }
         const double local = estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, false);
-        const double spread = estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, true);
+        const double spread = estimate(kv_sorted, p->n_rt, L, cus, setup, merge_per_row_split, R, true);
         *order = spread < local * 0.98 ? DDTV_ORDER_SPREAD : DDTV_ORDER_XCD_LOCAL;
         return std::min(local, spread);
     };
@@ -327,7 +349,9 @@ ddtv_status ddtv_build_visibility(const int32_t* parent, const int32_t* prefix_l
     v.bits = reinterpret_cast<uint32_t*>(base + L.bits);
     v.rows = reinterpret_cast<ddtv_row*>(base + L.rows);
     v.status = reinterpret_cast<int32_t*>(base + L.status);
+    v.order = reinterpret_cast<int32_t*>(base + L.order);
     v.prefix_host = prefix_len;
+    const std::vector<int> perm = longest_first(prefix_len, B);
 
     int64_t off = 0;
     for (int b0 = 0; b0 < B; b0 += kVisChunk) {
@@ -337,9 +361,11 @@ ddtv_status ddtv_build_visibility(const int32_t* parent, const int32_t* prefix_l
         for (int k = 0; k < nb; ++k) {
             ch.kv_off[k] = off;
             ch.prefix[k] = prefix_len[b0 + k];
+            ch.order[k] = perm[b0 + k];
             off += (int64_t)prefix_len[b0 + k] + Q;
         }
-        if (launch_visibility(parent, b0, nb, Q, v.W, v.bits, v.rows, v.status, ch, stream) != hipSuccess)
+        if (launch_visibility(parent, b0, nb, Q, v.W, v.bits, v.rows, v.status, v.order, ch, stream) !=
+            hipSuccess)
             return DDTV_EDEVICE;
     }
     *vis = v;
@@ -425,6 +451,7 @@ ddtv_status ddtv_verify_attn_ex(const float* q_abs, const float* q_rope, const v
     a.split_len = p.split_len;
     a.n_split = p.n_split;
     a.spread = p.order == DDTV_ORDER_SPREAD;
+    a.order = a.spread ? vis->order : nullptr;   // XCD-local keeps rows in their natural order
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 
     if (opts && opts->attn_begin && hipEventRecord(opts->attn_begin, stream) != hipSuccess) return DDTV_EDEVICE;

@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs a) {
     const int64_t w = work_item(a);
     const int rt = (int)(w % a.n_rt);
     const int s = (int)((w / a.n_rt) % a.n_split);
-    const int b = (int)(w / ((int64_t)a.n_rt * a.n_split));
+    const int b = batch_row(a, (int)(w / ((int64_t)a.n_rt * a.n_split)));
     const int kv_len = a.rows[b].kv_len;
     if (s * a.split_len >= kv_len) return;   // this batch row needs fewer splits
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

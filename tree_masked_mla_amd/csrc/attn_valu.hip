@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
     const int64_t w = work_item(a);
     const int rt = (int)(w % a.n_rt);
     const int s = (int)((w / a.n_rt) % a.n_split);
-    const int b = (int)(w / ((int64_t)a.n_rt * a.n_split));
+    const int b = batch_row(a, (int)(w / ((int64_t)a.n_rt * a.n_split)));
     const ddtv_row rowd = a.rows[b];
     const int kv_len = rowd.kv_len, P = rowd.prefix;
     const int n_b = (kv_len + a.split_len - 1) / a.split_len;

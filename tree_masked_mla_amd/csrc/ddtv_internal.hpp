@@ -27,6 +27,7 @@ struct AttnArgs {
     const void* k_rope;      // [total_kv][64]
     const uint32_t* bits;    // [B][Q][W]
     const ddtv_row* rows;    // [B]
+    const int32_t* order;    // [B] batch row of each grid slot, or null for the identity
     float* out;              // [B][Q][H][512]
     float* lse;              // [B][Q][H] or null
     float* part_o;           // [B][n_split][R][512]   (n_split > 1)
@@ -42,11 +43,12 @@ struct AttnArgs {
 struct VisChunk {
     int64_t kv_off[kVisChunk];
     int32_t prefix[kVisChunk];
+    int32_t order[kVisChunk];   // entries b0 .. b0+nb-1 of the longest-first row order
 };
 
 // Launchers (return the launch error, never synchronise).
 hipError_t launch_visibility(const int32_t* parent, int b0, int nb, int Q, int W, uint32_t* bits,
-                             ddtv_row* rows, int32_t* status, const VisChunk& chunk,
+                             ddtv_row* rows, int32_t* status, int32_t* order, const VisChunk& chunk,
                              hipStream_t stream);
 hipError_t launch_attn_valu(const AttnArgs& a, int kv_dtype, int64_t grid, hipStream_t stream);
 hipError_t launch_attn_mfma(const AttnArgs& a, int kv_dtype, int64_t grid, hipStream_t stream);
@@ -75,6 +77,9 @@ __host__ __device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t G) {
 __device__ __forceinline__ int64_t work_item(const AttnArgs& a) {
     return a.spread ? (int64_t)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
 }
+
+// Batch row of grid slot `slot` (the slowest-varying part of the work item).
+__device__ __forceinline__ int batch_row(const AttnArgs& a, int slot) { return a.order ? a.order[slot] : slot; }
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }

@@ -17,7 +17,8 @@ namespace ddtv {
 __global__ __launch_bounds__(256) void visibility_kernel(const int32_t* __restrict__ parent, int b0,
                                                          int Q, int W, uint32_t* __restrict__ bits,
                                                          ddtv_row* __restrict__ rows,
-                                                         int32_t* __restrict__ status, VisChunk chunk) {
+                                                         int32_t* __restrict__ status,
+                                                         int32_t* __restrict__ order, VisChunk chunk) {
     __shared__ uint32_t sbits[2][kMaxQ][kMaxW];
     __shared__ int32_t sjump[2][kMaxQ];
     __shared__ int32_t sbad;
@@ -70,15 +71,16 @@ __global__ __launch_bounds__(256) void visibility_kernel(const int32_t* __restri
         r.kv_len = chunk.prefix[lb] + Q;
         rows[b] = r;
         status[b] = (sbad < Q) ? sbad : -1;
+        order[b] = chunk.order[lb];
     }
 }
 
 hipError_t launch_visibility(const int32_t* parent, int b0, int nb, int Q, int W, uint32_t* bits,
-                             ddtv_row* rows, int32_t* status, const VisChunk& chunk,
+                             ddtv_row* rows, int32_t* status, int32_t* order, const VisChunk& chunk,
                              hipStream_t stream) {
     (void)hipGetLastError();   // report only this launch's error
     hipLaunchKernelGGL(visibility_kernel, dim3(nb), dim3(256), 0, stream, parent, b0, Q, W, bits,
-                       rows, status, chunk);
+                       rows, status, order, chunk);
     return hipGetLastError();
 }
 
