@@ -146,6 +146,25 @@ def test_workgroup_order_changes_nothing(path, kv_dtype):
     assert np.array_equal(res[0][1], res[1][1])
 
 
+def test_spread_order_many_rows_and_no_order_table():
+    """70 ragged batch rows, several KV splits: S1 writes the longest-first row
+    table over two launches (up to 64 rows each), and the spread grid visits rows
+    through it.  A visibility struct without the table (a caller-made one) runs
+    rows in their natural order.
+    All three give bit-identical results, equal to the oracle."""
+    rng = np.random.default_rng(4170)
+    w = wl.make_workload("rows70", 4170, B=70, H=4, Q=8, prefix=[int(x) for x in rng.integers(0, 300, 70)],
+                         tree="uniform")
+    r1, o1, l1 = check_full(w, split_len=96, what="rows70 local", wg_order=1)
+    r2, o2, l2 = check_full(w, split_len=96, what="rows70 spread", wg_order=2)
+    assert r2.plan()[5] == 2 and r2.plan()[3] > 1
+    r2.vis.vis.order = None                      # drop the row-order table
+    r2.verify()
+    o3, l3 = r2.results()
+    for o, l in ((o2, l2), (o3, l3)):
+        assert np.array_equal(o, o1) and np.array_equal(l, l1)
+
+
 # ----------------------------------------------------------------------------- edge cases
 @pytest.mark.parametrize("path", [1, 2])
 @pytest.mark.parametrize("B,H,Q,prefix", [
