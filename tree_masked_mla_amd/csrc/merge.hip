@@ -10,16 +10,16 @@
 //
 // 128 threads per query row (one float4 of the 512-d output each), 2 rows per
 // workgroup.  Rows whose batch row needed a single split were finished by the
-// attention kernel and are skipped.  The split statistics and partial outputs are
-// read in batches of kBatch independent loads, so a row costs a few memory round
-// trips instead of two per split.
+// attention kernel and are skipped.  The splits are read in batches of kBatch
+// independent loads and folded in with an online rescale (the running maximum
+// moves batch by batch), so up to kBatch splits cost one memory round trip.
 #include "ddtv_internal.hpp"
 
 namespace ddtv {
 
 namespace {
 
-constexpr int kBatch = 8;
+constexpr int kBatch = 16;
 
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
     const int64_t gr = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);   // b * R + row
@@ -34,39 +34,39 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
     const int64_t pbase = (int64_t)b * a.n_split * a.R + row;   // split s at pbase + s * R
     const float4* po = reinterpret_cast<const float4*>(a.part_o);
 
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < n_b; s0 += kBatch) {
-        float mx[kBatch];
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k)
-            mx[k] = (s0 + k < n_b) ? a.part_ml[pbase + (int64_t)(s0 + k) * a.R].x : -INFINITY;
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) M = fmaxf(M, mx[k]);
-    }
-    float L = 0.f;
+    float M = -INFINITY, L = 0.f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (M != -INFINITY) {
-        for (int s0 = 0; s0 < n_b; s0 += kBatch) {
-            float2 ml[kBatch];
-            float4 v[kBatch];
+    for (int s0 = 0; s0 < n_b; s0 += kBatch) {
+        float2 ml[kBatch];
+        float4 v[kBatch];
 #pragma unroll
-            for (int k = 0; k < kBatch; ++k) {
-                const bool in = s0 + k < n_b;
-                const int64_t p = pbase + (int64_t)(in ? s0 + k : 0) * a.R;
-                ml[k] = in ? a.part_ml[p] : make_float2(-INFINITY, 0.f);
-                v[k] = in ? po[p * 128 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-#pragma unroll
-            for (int k = 0; k < kBatch; ++k) {
-                // an empty split (m = -inf) has l = 0 and o = 0: weight 0
-                const float wgt = (ml[k].x == -INFINITY) ? 0.f : exp2f(ml[k].x - M);
-                L = fmaf(wgt, ml[k].y, L);
-                o.x = fmaf(wgt, v[k].x, o.x);
-                o.y = fmaf(wgt, v[k].y, o.y);
-                o.z = fmaf(wgt, v[k].z, o.z);
-                o.w = fmaf(wgt, v[k].w, o.w);
-            }
+        for (int k = 0; k < kBatch; ++k) {
+            const bool in = s0 + k < n_b;
+            const int64_t p = pbase + (int64_t)(in ? s0 + k : 0) * a.R;
+            ml[k] = in ? a.part_ml[p] : make_float2(-INFINITY, 0.f);
+            v[k] = in ? po[p * 128 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+        float Mb = M;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) Mb = fmaxf(Mb, ml[k].x);
+        if (Mb == -INFINITY) continue;          // nothing visible so far
+        // an empty split (m = -inf) has l = 0 and o = 0: weight 0
+        const float r = (M == -INFINITY) ? 0.f : exp2f(M - Mb);
+        L *= r;
+        o.x *= r;
+        o.y *= r;
+        o.z *= r;
+        o.w *= r;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const float wgt = (ml[k].x == -INFINITY) ? 0.f : exp2f(ml[k].x - Mb);
+            L = fmaf(wgt, ml[k].y, L);
+            o.x = fmaf(wgt, v[k].x, o.x);
+            o.y = fmaf(wgt, v[k].y, o.y);
+            o.z = fmaf(wgt, v[k].z, o.z);
+            o.w = fmaf(wgt, v[k].w, o.w);
+        }
+        M = Mb;
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     reinterpret_cast<float4*>(a.out)[gr * 128 + c] = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
