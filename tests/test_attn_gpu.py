@@ -6,6 +6,8 @@ Small and reduced workloads are compared in full; the full-size dense workloads
 run in the launch configuration the benchmark times and are compared on a
 seeded sample of rows (plus properties that hold for every row).
 """
+import functools
+
 import numpy as np
 import pytest
 
@@ -263,6 +265,29 @@ def _full_sampled(name, n_rows):
     e = assert_close(out[rows], ref, w.kv_dtype, name)
     assert_lse_close(lse[rows], rlse, w.kv_dtype, name)
     say(f"  {name}: max abs err {e:.2e} on {len(rows)} sampled rows")
+
+
+@functools.lru_cache(maxsize=1)
+def _beyond_2gib():
+    return wl.make_workload("big", 4600, B=2, H=16, Q=16, prefix=[600000, 600000], tree="uniform")
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_fp32_cache_beyond_2gib(path):
+    """Two 600k-position batch rows: the fp32 latent cache spans 2.46 GB, so the
+    second row's cache reaches byte offsets past 2^31.  Sampled query rows of both
+    batch rows against the oracle."""
+    say("generate beyond-2GiB workload")
+    w = _beyond_2gib()
+    assert w.ckv.nbytes > 2**31
+    bits, _, _ = oracle.build_visibility(w.parent)
+    r, out, lse = run(w, path=path)
+    say(f"  plan {r.plan()}")
+    rows = np.array([0, 37, 255, 256, 300, 511], dtype=np.int64)   # both batch rows, first and last nodes
+    ref, rlse = oracle_rows(w, bits, rows, chunk=1)
+    e = assert_close(out[rows], ref, 0, f"beyond 2 GiB path {path}")
+    assert_lse_close(lse[rows], rlse, 0, f"beyond 2 GiB path {path}")
+    say(f"  max abs err {e:.2e}")
 
 
 def test_c4_full_sampled():
