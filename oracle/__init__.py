@@ -4,6 +4,8 @@ TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg may import this package; the product library never does.  The
 arithmetic lives in ``ddtv_oracle.c`` (plain fp64 C, single-threaded); this file
 only compiles it with gcc, marshals numpy arrays and returns numpy results.
+The best-first draft-tree builder's oracle lives in ``ddtv_tree_oracle.c``
+(plain C, a binary heap), compiled into the same library.
 """
 from __future__ import annotations
 
@@ -15,6 +17,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ddtv_oracle.c")
+_SRC_TREE = os.path.join(_HERE, "ddtv_tree_oracle.c")
 _LIB = os.path.join(_HERE, "libddtv_oracle.so")
 
 REF_OK, REF_EINVAL, REF_ETREE = 0, 1, 2
@@ -28,7 +31,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall",
-                               "-Wextra", "-o", tmp, _SRC, "-lm"])
+                               "-Wextra", "-o", tmp, _SRC, _SRC_TREE, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -43,6 +46,10 @@ def configure(lib):
     lib.ddtvref_row_probs.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, f64, i64, P]
     lib.ddtvref_partial.argtypes = [P, P, P, P, i32, P, i64, f64, P, P, P]
     lib.ddtvref_merge.argtypes = [i32, P, P, P, P, P]
+    lib.ddtvref_build_tree_row.argtypes = [P, P, i32, i32, i32, P, P, P, P, P]
+    lib.ddtvref_build_tree_row.restype = ctypes.c_int
+    lib.ddtvref_tree_capacity.argtypes = [i32, i32, i64]
+    lib.ddtvref_tree_capacity.restype = i64
     for name in ("ddtvref_build_visibility", "ddtvref_verify_attn_rows",
                  "ddtvref_row_probs", "ddtvref_partial", "ddtvref_merge", "ddtvref_words"):
         getattr(lib, name).restype = ctypes.c_int
@@ -52,7 +59,8 @@ def configure(lib):
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(os.path.getmtime(_SRC),
+                                                                       os.path.getmtime(_SRC_TREE)):
             build()
         _lib = configure(ctypes.CDLL(_LIB))
     return _lib
@@ -162,3 +170,28 @@ def attend_workload(w, rows=None, bits=None):
         bits, _, _ = build_visibility(w.parent)
     return verify_attn(w.q_abs, w.q_rope, w.ckv, w.k_rope, w.kv_dtype, w.prefix, bits,
                        w.scale, rows=rows)
+
+
+def tree_capacity(D: int, K: int, cap: int = 1 << 40) -> int:
+    """Nodes of the full K-ary tree of depth D (saturated at cap)."""
+    return int(_load().ddtvref_tree_capacity(D, K, cap))
+
+
+def build_tree(logp: np.ndarray, Q: int, tokens: np.ndarray | None = None):
+    """Best-first draft trees of Q nodes from per-depth top-K log-probs.
+
+    logp: float32 [B][D][K] (each [b][d] sorted descending); tokens: int32 [B][D][K] or None.
+    Returns (rc, dict of int32/float32 [B][Q] arrays: parent, depth, rank, token, score)."""
+    lib = _load()
+    logp = _c(logp, np.float32)
+    B, D, K = logp.shape
+    tok = None if tokens is None else _c(tokens, np.int32)
+    out = {k: np.zeros((B, Q), np.int32) for k in ("parent", "depth", "rank", "token")}
+    out["score"] = np.zeros((B, Q), np.float32)
+    for b in range(B):
+        rc = lib.ddtvref_build_tree_row(_p(logp[b]), _p(None if tok is None else tok[b]), D, K, Q,
+                                        _p(out["parent"][b]), _p(out["depth"][b]), _p(out["rank"][b]),
+                                        _p(out["token"][b]), _p(out["score"][b]))
+        if rc != REF_OK:
+            return rc, None
+    return REF_OK, out

@@ -14,8 +14,10 @@ import pytest
 
 import oracle
 import test_oracle_pins as pins
+import test_tree_oracle as tree_pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ddtv_oracle.c")
+SRC_TREE = os.path.join(os.path.dirname(oracle.__file__), "ddtv_tree_oracle.c")
 
 # (id, original text, mutated text)
 MUTATIONS = [
@@ -59,25 +61,64 @@ PINS = [
 ]
 
 
-@pytest.mark.parametrize("mid,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_pins_catch_mutation(tmp_path, mid, old, new):
-    src = open(SRC).read()
+# Mistakes planted in the best-first tree builder's oracle.
+TREE_MUTATIONS = [
+    ("sibling_scored_from_itself", "float s = node_score[c.parent] + logp[(c.depth - 1) * K + c.rank + 1];",
+     "float s = c.score + logp[(c.depth - 1) * K + c.rank + 1];"),
+    ("child_reads_wrong_depth", "float s = c.score + logp[c.depth * K + 0];",
+     "float s = c.score + logp[(c.depth > 0 ? c.depth - 1 : 0) * K + 0];"),
+    ("worst_first", "if (a->score != b->score) return a->score > b->score;",
+     "if (a->score != b->score) return a->score < b->score;"),
+    ("ties_later_parent_first", "if (a->parent != b->parent) return a->parent < b->parent;",
+     "if (a->parent != b->parent) return a->parent > b->parent;"),
+    ("siblings_skip_last", "if (c.depth >= 1 && c.rank + 1 < K) {", "if (c.depth >= 1 && c.rank + 2 < K) {"),
+    ("depth_cap_one_short", "if (c.depth < D) {", "if (c.depth < D - 1) {"),
+    ("child_parented_to_grandparent", "Cand ch = {s, i, c.depth + 1, 0};", "Cand ch = {s, c.parent < 0 ? i : c.parent, c.depth + 1, 0};"),
+]
+
+TREE_PINS = [
+    lambda: tree_pins.test_bruteforce_top_scores(3, 3, 20),
+    lambda: tree_pins.test_bruteforce_top_scores(5, 3, 60),
+    tree_pins.test_tree_invariants,
+    tree_pins.test_k1_is_a_chain_and_d1_is_a_star,
+    lambda: tree_pins.test_matches_offering_all_children(0),
+    tree_pins.test_ties_go_to_the_earlier_parent_then_rank,
+]
+
+
+def _run_mutation(tmp_path, target, mid, old, new, pins_to_run):
+    """Compile the oracle with one planted mistake in `target`; return the pins that fail."""
+    src = open(target).read()
     assert src.count(old) >= 1, f"mutation anchor for {mid} not found"
     mutated = src.replace(old, new, 1)
-    c = tmp_path / "mut.c"
+    c = tmp_path / ("mut_" + os.path.basename(target))
     so = tmp_path / "libmut.so"
     c.write_text(mutated)
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", str(so), str(c), "-lm"])
+    sources = [str(c) if f == target else f for f in (SRC, SRC_TREE)]
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", str(so), *sources, "-lm"])
     lib = oracle.configure(ctypes.CDLL(str(so)))
     saved = oracle._lib
     oracle._lib = lib
     failed = []
     try:
-        for pin in PINS:
+        for pin in pins_to_run:
             try:
                 pin()
             except (AssertionError, ValueError):
                 failed.append(getattr(pin, "__name__", "lambda"))
     finally:
         oracle._lib = saved
+    return failed
+
+
+@pytest.mark.parametrize("mid,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_mutation(tmp_path, mid, old, new):
+    failed = _run_mutation(tmp_path, SRC, mid, old, new, PINS)
     assert failed, f"no pin caught mutation {mid}"
+
+
+@pytest.mark.parametrize("mid,old,new", TREE_MUTATIONS, ids=[m[0] for m in TREE_MUTATIONS])
+def test_tree_pins_catch_mutation(tmp_path, mid, old, new):
+    failed = _run_mutation(tmp_path, SRC_TREE, mid, old, new, TREE_PINS)
+    assert failed, f"no pin caught mutation {mid}"
+
