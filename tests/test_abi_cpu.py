@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert dd.ddtv_version() == 300
+    assert dd.ddtv_version() == 400
     for code in range(6):
         assert dd.ddtv_status_string(code)
     assert dd.ddtv_status_string(2).startswith("malformed tree")
@@ -135,6 +135,27 @@ def test_verify_host_errors(lib):
     assert verify_call(lib, vis, H=16, opts=opts) == dd.DDTV_EWORKSPACE
     assert verify_call(lib, vis, H=16, opts=opts, ws=FAKE, ws_bytes=need - 1) == dd.DDTV_EWORKSPACE
     assert verify_call(lib, vis, H=16, opts=opts, ws=FAKE + 16, ws_bytes=need) == E
+
+
+def test_build_tree_argument_checks(lib):
+    """The tree builder's host checks come before any HIP call (so no GPU is touched here)."""
+    E, U = dd.DDTV_EINVAL, dd.DDTV_EUNSUPPORTED
+
+    def call(logp=FAKE, tokens=None, B=2, D=3, K=4, Q=20, parent=FAKE + 4096, depth=None):
+        return lib.ddtv_build_tree(logp, tokens, B, D, K, Q, parent, depth, None, None, None, None)
+
+    assert call(logp=None) == E
+    assert call(parent=None) == E
+    assert call(parent=FAKE + 2) == E                 # misaligned
+    assert call(depth=FAKE + 6) == E
+    assert call(B=0) == E
+    assert call(D=0) == E
+    assert call(Q=0) == E
+    assert call(Q=257) == E
+    assert call(K=0) == U
+    assert call(K=65) == U
+    assert call(D=2, K=2, Q=8) == E                   # the depth-2 binary tree has 7 nodes
+    assert call(D=1, K=64, Q=66) == E
 
 
 def test_plan_rules(lib):

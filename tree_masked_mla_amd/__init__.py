@@ -27,7 +27,7 @@ D_LATENT, D_ROPE, MAX_Q = 512, 64, 256
 EXPORTED = (
     "ddtv_vis_bytes", "ddtv_build_visibility", "ddtv_read_status", "ddtv_workspace_bytes",
     "ddtv_workspace_bytes_ex", "ddtv_verify_attn", "ddtv_verify_attn_ex", "ddtv_plan_info",
-    "ddtv_status_string", "ddtv_version",
+    "ddtv_status_string", "ddtv_version", "ddtv_build_tree",
 )
 
 
@@ -83,6 +83,8 @@ def load(path: str = LIB_PATH):
     lib.ddtv_plan_info.argtypes = [VP, i32, ctypes.c_int, OP, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                    ctypes.POINTER(i32), ctypes.POINTER(i64), ctypes.POINTER(i32)]
     lib.ddtv_plan_info.restype = ctypes.c_int
+    lib.ddtv_build_tree.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P, P]
+    lib.ddtv_build_tree.restype = ctypes.c_int
     lib.ddtv_status_string.argtypes = [ctypes.c_int]
     lib.ddtv_status_string.restype = ctypes.c_char_p
     lib.ddtv_version.argtypes = []
@@ -185,6 +187,14 @@ def ddtv_plan_info(vis: Visibility, H: int, kv_dtype: int, opts: ddtv_opts | Non
                                ctypes.byref(p), ctypes.byref(L), ctypes.byref(ns), ctypes.byref(wg),
                                ctypes.byref(order))
     return rc, p.value, L.value, ns.value, wg.value, order.value
+
+
+def ddtv_build_tree(logp, Q: int, parent, tokens=None, depth=None, rank=None, token=None, score=None,
+                    stream=None) -> int:
+    """logp: device float32 [B][D][K]; outputs: device [B][Q] tensors (parent required)."""
+    B, D, K = (int(x) for x in logp.shape)
+    return load().ddtv_build_tree(_ptr(logp), _ptr(tokens), B, D, K, Q, _ptr(parent), _ptr(depth), _ptr(rank),
+                                  _ptr(token), _ptr(score), _stream(stream))
 
 
 def ddtv_verify_attn(q_abs, q_rope, ckv, k_rope, kv_dtype: int, H: int, vis: Visibility, scale: float, out,

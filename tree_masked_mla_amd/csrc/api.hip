@@ -17,7 +17,7 @@ using namespace ddtv;
 
 namespace {
 
-constexpr int32_t kVersion = 300;   // 0.3.0: workgroup order (XCD-local or spread) in the plan
+constexpr int32_t kVersion = 400;   // 0.4.0: best-first draft-tree builder
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -370,6 +370,37 @@ ddtv_status ddtv_build_visibility(const int32_t* parent, const int32_t* prefix_l
     }
     *vis = v;
     return DDTV_OK;
+}
+
+ddtv_status ddtv_build_tree(const float* logp, const int32_t* tokens, int32_t B, int32_t D, int32_t K, int32_t Q,
+                            int32_t* parent, int32_t* depth, int32_t* rank, int32_t* token, float* score,
+                            hipStream_t stream) {
+    if (!logp || !parent) return DDTV_EINVAL;
+    if (!aligned(logp, 4) || !aligned(parent, 4) || !aligned(tokens, 4) || !aligned(depth, 4) ||
+        !aligned(rank, 4) || !aligned(token, 4) || !aligned(score, 4))
+        return DDTV_EINVAL;
+    if (B < 1 || D < 1 || Q < 1 || Q > kMaxQ) return DDTV_EINVAL;
+    if (K < 1 || K > kMaxTreeK) return DDTV_EUNSUPPORTED;
+    // nodes of the full K-ary tree of depth D, counted until they reach Q
+    int64_t nodes = 1, level = 1;
+    for (int d = 1; d <= D && nodes < Q; ++d) {
+        level = std::min<int64_t>(level * K, (int64_t)kMaxQ + 1);
+        nodes += level;
+    }
+    if (nodes < Q) return DDTV_EINVAL;
+    TreeArgs a;
+    a.logp = logp;
+    a.tokens = tokens;
+    a.parent = parent;
+    a.depth = depth;
+    a.rank = rank;
+    a.token = token;
+    a.score = score;
+    a.B = B;
+    a.D = D;
+    a.K = K;
+    a.Q = Q;
+    return launch_tree_build(a, stream) == hipSuccess ? DDTV_OK : DDTV_EDEVICE;
 }
 
 ddtv_status ddtv_read_status(const ddtv_vis* vis, int32_t* bad_row, int32_t* bad_node, hipStream_t stream) {

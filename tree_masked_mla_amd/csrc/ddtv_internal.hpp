@@ -40,6 +40,19 @@ struct AttnArgs {
     float scale_log2;        // scale * log2(e)
 };
 
+// Everything the draft-tree builder needs (passed by value).
+struct TreeArgs {
+    const float* logp;       // [B][D][K], sorted descending within each [b][d]
+    const int32_t* tokens;   // [B][D][K] or null
+    int32_t* parent;         // [B][Q]
+    int32_t* depth;          // [B][Q] or null
+    int32_t* rank;           // [B][Q] or null
+    int32_t* token;          // [B][Q] or null
+    float* score;            // [B][Q] or null
+    int B, D, K, Q;
+};
+constexpr int kMaxTreeK = 64;   // choices per depth the builder accepts
+
 struct VisChunk {
     int64_t kv_off[kVisChunk];
     int32_t prefix[kVisChunk];
@@ -56,6 +69,7 @@ int mfma_rows_per_workgroup(int kv_dtype);   // query rows per workgroup of the 
 hipError_t launch_attn_mfma_bf16(const AttnArgs& a, int64_t grid, hipStream_t stream);
 int bf16_rows_per_workgroup();   // query rows per workgroup of the bf16 MFMA kernel
 hipError_t launch_merge(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_tree_build(const TreeArgs& a, hipStream_t stream);
 
 constexpr int kValuRows = 16;   // query rows per VALU workgroup
 

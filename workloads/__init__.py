@@ -259,6 +259,19 @@ def c2_chain() -> Workload:
     return w.with_parent(np.stack([chain_tree(w.Q) for _ in range(w.B)]), name="c2-chain")
 
 
+def drafter_topk(seed: int, B: int, D: int, K: int, vocab: int = 32, sigma: float = 2.0):
+    """Synthetic drafter output for the tree builder: for each batch row and depth,
+    logits ~ N(0, sigma^2) over `vocab` tokens, their log-softmax, and the K best
+    (log-probability float32 [B][D][K] sorted descending, token id int32 [B][D][K])."""
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((B, D, vocab)) * sigma
+    lp = logits - np.log(np.exp(logits - logits.max(-1, keepdims=True)).sum(-1, keepdims=True)) \
+        - logits.max(-1, keepdims=True)
+    order = np.argsort(-lp, axis=-1, kind="stable")[..., :K]
+    return (np.ascontiguousarray(np.take_along_axis(lp, order, -1), dtype=np.float32),
+            np.ascontiguousarray(order, dtype=np.int32))
+
+
 def sample_rows(w: Workload, n: int, seed: int = 7) -> np.ndarray:
     """Seeded sample of n flat query-row ids (b*Q + q)*H + h spread over all batch rows."""
     rng = np.random.default_rng(seed)
