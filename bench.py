@@ -120,6 +120,34 @@ def load_traffic(config_name, kernel_hash):
 
 
 # ----------------------------------------------------------------------------- CPU baseline (oracle)
+def time_tree_builder(dd, hip, stream, dev, B, Q, D=12, K=4, steps=20, warmup=3):
+    """The draft-tree builder (ddtv_build_tree) on B trees of Q nodes from synthetic
+    drafter top-K log-probs: average launch time from HIP events on the launch stream."""
+    import torch
+    import workloads as wl
+    lp, tok = wl.drafter_topk(7000 + B + Q, B, D, K)
+    lp_d = torch.from_numpy(lp).to(dev)
+    tok_d = torch.from_numpy(tok).to(dev)
+    outs = [torch.empty((B, Q), dtype=torch.int32, device=dev) for _ in range(4)]
+    score = torch.empty((B, Q), dtype=torch.float32, device=dev)
+
+    def launch():
+        rc = dd.ddtv_build_tree(lp_d, Q, outs[0], tokens=tok_d, depth=outs[1], rank=outs[2], token=outs[3],
+                                score=score, stream=stream)
+        assert rc == dd.DDTV_OK, rc
+    for _ in range(warmup):
+        launch()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for _ in range(steps):
+        launch()
+    hip.record(e1, stream)
+    us = hip.elapsed_ms(e0, e1) * 1e3 / steps
+    return {"workload": f"B={B} trees of Q={Q} nodes, depth <= {D}, top-{K} per depth (synthetic drafter)",
+            "us_per_launch": round(us, 2), "ns_per_node": round(us * 1e3 / Q, 1), "launches": steps,
+            "note": "one wave per tree, one node per step: bound by the dependent chain of Q steps"}
+
+
 def cpu_baseline(w, budget_s=15.0, max_rows=4096):
     """The oracle (single-threaded fp64 C) on a seeded sample of query rows of the
     same workload, for about budget_s seconds.  Reported as tree-query tokens/s
@@ -269,6 +297,7 @@ def main():
             "kernel_source_hash": khash,
         },
     }
+    out["tree_build"] = time_tree_builder(dd, hip, stream, dev, w.B, w.Q)
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(w, budget_s=args.cpu_budget)
