@@ -5,7 +5,8 @@ CPU-baseline leg may import this package; the product library never does.  The
 arithmetic lives in ``ddtv_oracle.c`` (plain fp64 C, single-threaded); this file
 only compiles it with gcc, marshals numpy arrays and returns numpy results.
 The best-first draft-tree builder's oracle lives in ``ddtv_tree_oracle.c``
-(plain C, a binary heap), compiled into the same library.
+(plain C, a binary heap) and the greedy tree-accept step's in
+``ddtv_accept_oracle.c``, compiled into the same library.
 """
 from __future__ import annotations
 
@@ -18,6 +19,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ddtv_oracle.c")
 _SRC_TREE = os.path.join(_HERE, "ddtv_tree_oracle.c")
+_SRC_ACCEPT = os.path.join(_HERE, "ddtv_accept_oracle.c")
+SOURCES = (_SRC, _SRC_TREE, _SRC_ACCEPT)
 _LIB = os.path.join(_HERE, "libddtv_oracle.so")
 
 REF_OK, REF_EINVAL, REF_ETREE = 0, 1, 2
@@ -31,7 +34,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall",
-                               "-Wextra", "-o", tmp, _SRC, _SRC_TREE, "-lm"])
+                               "-Wextra", "-o", tmp, *SOURCES, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -50,6 +53,10 @@ def configure(lib):
     lib.ddtvref_build_tree_row.restype = ctypes.c_int
     lib.ddtvref_tree_capacity.argtypes = [i32, i32, i64]
     lib.ddtvref_tree_capacity.restype = i64
+    lib.ddtvref_tree_accept_row.argtypes = [P, i32, P, P, i32, P, P, P, P]
+    lib.ddtvref_tree_accept_row.restype = ctypes.c_int
+    lib.ddtvref_compact_rows.argtypes = [P, P, i64, i64, i32, P, i32]
+    lib.ddtvref_compact_rows.restype = None
     for name in ("ddtvref_build_visibility", "ddtvref_verify_attn_rows",
                  "ddtvref_row_probs", "ddtvref_partial", "ddtvref_merge", "ddtvref_words"):
         getattr(lib, name).restype = ctypes.c_int
@@ -59,8 +66,7 @@ def configure(lib):
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(os.path.getmtime(_SRC),
-                                                                       os.path.getmtime(_SRC_TREE)):
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(os.path.getmtime(f) for f in SOURCES):
             build()
         _lib = configure(ctypes.CDLL(_LIB))
     return _lib
@@ -195,3 +201,37 @@ def build_tree(logp: np.ndarray, Q: int, tokens: np.ndarray | None = None):
         if rc != REF_OK:
             return rc, None
     return REF_OK, out
+
+
+def tree_accept(logits: np.ndarray, parent: np.ndarray, token: np.ndarray):
+    """Greedy acceptance of B verified trees.
+
+    logits: float32 [B][Q][V] (the target's logits after each node); parent, token: int32 [B][Q].
+    Returns (rc, dict: pred, path, out_tokens int32 [B][Q]; accept_len int32 [B])."""
+    lib = _load()
+    logits = _c(logits, np.float32)
+    parent = _c(parent, np.int32)
+    token = _c(token, np.int32)
+    B, Q, V = logits.shape
+    out = {k: np.zeros((B, Q), np.int32) for k in ("pred", "path", "out_tokens")}
+    out["accept_len"] = np.zeros(B, np.int32)
+    for b in range(B):
+        k = ctypes.c_int32()
+        rc = lib.ddtvref_tree_accept_row(_p(logits[b]), V, _p(parent[b]), _p(token[b]), Q, _p(out["pred"][b]),
+                                         _p(out["path"][b]), _p(out["out_tokens"][b]), ctypes.byref(k))
+        if rc != REF_OK:
+            return rc, None
+        out["accept_len"][b] = k.value
+    return REF_OK, out
+
+
+def compact_rows(rows: np.ndarray, prefix: int, path: np.ndarray, k: int) -> np.ndarray:
+    """One batch row's cache rows after acceptance (a new array): row prefix + j
+    takes row prefix + path[j] for j = 1..k.  rows: [n_rows][...] any dtype."""
+    src = np.ascontiguousarray(rows)
+    dst = np.empty_like(src)
+    n = src.shape[0]
+    row_bytes = src.nbytes // max(n, 1)
+    _load().ddtvref_compact_rows(_p(src.view(np.uint8)), _p(dst.view(np.uint8)), n, row_bytes, prefix,
+                                 _p(_c(path, np.int32)), k)
+    return dst

@@ -10,14 +10,17 @@ import ctypes
 import os
 import subprocess
 
+import numpy as np
 import pytest
 
 import oracle
 import test_oracle_pins as pins
+import test_accept_oracle as accept_pins
 import test_tree_oracle as tree_pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ddtv_oracle.c")
 SRC_TREE = os.path.join(os.path.dirname(oracle.__file__), "ddtv_tree_oracle.c")
+SRC_ACCEPT = os.path.join(os.path.dirname(oracle.__file__), "ddtv_accept_oracle.c")
 
 # (id, original text, mutated text)
 MUTATIONS = [
@@ -76,6 +79,25 @@ TREE_MUTATIONS = [
     ("child_parented_to_grandparent", "Cand ch = {s, i, c.depth + 1, 0};", "Cand ch = {s, c.parent < 0 ? i : c.parent, c.depth + 1, 0};"),
 ]
 
+# Mistakes planted in the tree-accept / compaction oracle.
+ACCEPT_MUTATIONS = [
+    ("argmax_last_on_ties", "if (row[v] > row[best]) best = v;", "if (row[v] >= row[best]) best = v;"),
+    ("walk_uses_child_prediction", "if (parent[c] == cur && token[c] == pred[cur]) {",
+     "if (parent[c] == cur && token[c] == pred[c]) {"),
+    ("last_matching_child", "                next = c;\n                break;", "                next = c;"),
+    ("bonus_from_root", "out_tokens[k] = pred[cur];", "out_tokens[k] = pred[0];"),
+    ("no_bonus", "out_tokens[k] = pred[cur];", ""),
+    ("compaction_off_by_one", "memcpy(dst + (int64_t)(prefix + j) * row_bytes", "memcpy(dst + (int64_t)(prefix + j - 1) * row_bytes"),
+    ("compaction_moves_root", "for (int32_t j = 1; j <= k; ++j)", "for (int32_t j = 0; j < k; ++j)"),
+]
+
+ACCEPT_PINS = [
+    lambda: accept_pins.test_walk_equals_matching_edge_set(1, 6, 32),
+    lambda: accept_pins.test_walk_equals_matching_edge_set(2, 4, 128),
+    accept_pins.test_special_cases,
+    lambda: accept_pins.test_compaction_equals_fancy_indexing(np.float32),
+]
+
 TREE_PINS = [
     lambda: tree_pins.test_bruteforce_top_scores(3, 3, 20),
     lambda: tree_pins.test_bruteforce_top_scores(5, 3, 60),
@@ -94,7 +116,7 @@ def _run_mutation(tmp_path, target, mid, old, new, pins_to_run):
     c = tmp_path / ("mut_" + os.path.basename(target))
     so = tmp_path / "libmut.so"
     c.write_text(mutated)
-    sources = [str(c) if f == target else f for f in (SRC, SRC_TREE)]
+    sources = [str(c) if f == target else f for f in (SRC, SRC_TREE, SRC_ACCEPT)]
     subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", str(so), *sources, "-lm"])
     lib = oracle.configure(ctypes.CDLL(str(so)))
     saved = oracle._lib
@@ -122,3 +144,9 @@ def test_tree_pins_catch_mutation(tmp_path, mid, old, new):
     failed = _run_mutation(tmp_path, SRC_TREE, mid, old, new, TREE_PINS)
     assert failed, f"no pin caught mutation {mid}"
 
+
+
+@pytest.mark.parametrize("mid,old,new", ACCEPT_MUTATIONS, ids=[m[0] for m in ACCEPT_MUTATIONS])
+def test_accept_pins_catch_mutation(tmp_path, mid, old, new):
+    failed = _run_mutation(tmp_path, SRC_ACCEPT, mid, old, new, ACCEPT_PINS)
+    assert failed, f"no pin caught mutation {mid}"
