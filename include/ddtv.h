@@ -260,6 +260,44 @@ ddtv_status ddtv_plan_info(const ddtv_vis *vis, int32_t H, ddtv_dtype kv_dtype,
                            const ddtv_opts *opts, int32_t *path, int32_t *split_len,
                            int32_t *n_split, int64_t *workgroups, int32_t *wg_order);
 
+/*
+ * Greedy tree acceptance after the verify step, then (optionally) the cache
+ * compaction that drops the unaccepted branches.
+ *   Pages: "The Moment of Truth: Validating a Custom CUDA Attention Kernel for
+ *   Speculative Decoding", section "Context: Building a Native DDTree Inference
+ *   Engine" (a greedy walk that decides which tree tokens are accepted); "The
+ *   Architecture of an Inference Engine: Designing the Model Structure for DDTree
+ *   Speculative Decoding", section "Input Knowledge Required" (the KV cache is
+ *   compacted after acceptance).  The rule implemented:
+ *   - pred[b][i] = argmax over v of logits[b][i][v] (float32; lowest index among
+ *     equal maxima): the target's token after node i's path;
+ *   - from the root, move to the lowest-index child whose draft token equals the
+ *     current node's prediction; stop where there is none.  k = the number of
+ *     moves (accepted draft tokens);
+ *   - path[b][0..k] = the accepted nodes, root first, then -1;
+ *     out_tokens[b][0..k] = the accepted nodes' draft tokens, then the last
+ *     accepted node's prediction (the bonus token), then -1; accept_len[b] = k;
+ *   - with ckv/k_rope: cache row prefix + path[j] of batch row b is copied to row
+ *     prefix + j, j = 1..k, in place (rows at kv_off + prefix + node, as for the
+ *     verify step); other rows are left as they are.
+ *
+ *   logits      DEVICE float [B][Q][V]; V >= 1
+ *   parent      DEVICE int32 [B][Q], the trees that were verified (well formed:
+ *               a malformed tree gives a walk over whatever its parents say)
+ *   token       DEVICE int32 [B][Q] draft token of each node (token[b][0] unused)
+ *   vis         HOST struct from ddtv_build_visibility for these trees (B, Q and
+ *               the device row table give the cache geometry)
+ *   ckv, k_rope DEVICE caches to compact (16-byte aligned), both or neither
+ *   kv_dtype    their element type
+ *   pred, path, out_tokens  DEVICE int32 [B][Q] out;  accept_len DEVICE int32 [B] out
+ * Errors: DDTV_EINVAL (null or misaligned pointers, V < 1, one cache without the
+ * other, a bad vis), DDTV_EUNSUPPORTED (dtype), DDTV_EDEVICE.
+ */
+ddtv_status ddtv_tree_accept(const float *logits, int32_t V, const int32_t *parent,
+                             const int32_t *token, const ddtv_vis *vis, void *ckv, void *k_rope,
+                             ddtv_dtype kv_dtype, int32_t *pred, int32_t *path,
+                             int32_t *out_tokens, int32_t *accept_len, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *ddtv_status_string(ddtv_status s);
 

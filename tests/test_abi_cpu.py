@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert dd.ddtv_version() == 400
+    assert dd.ddtv_version() == 500
     for code in range(6):
         assert dd.ddtv_status_string(code)
     assert dd.ddtv_status_string(2).startswith("malformed tree")
@@ -156,6 +156,25 @@ def test_build_tree_argument_checks(lib):
     assert call(K=65) == U
     assert call(D=2, K=2, Q=8) == E                   # the depth-2 binary tree has 7 nodes
     assert call(D=1, K=64, Q=66) == E
+
+
+def test_tree_accept_argument_checks(lib):
+    """Host checks of the accept step come before any HIP call."""
+    E, U = dd.DDTV_EINVAL, dd.DDTV_EUNSUPPORTED
+    vis = fake_vis(B=2, Q=9)
+
+    def call(logits=FAKE, V=32, v=vis, ckv=None, k_rope=None, dtype=0, pred=FAKE + 4096, accept_len=FAKE + 8192):
+        return lib.ddtv_tree_accept(logits, V, FAKE, FAKE, ctypes.byref(v.vis) if v is not None else None, ckv,
+                                    k_rope, dtype, pred, FAKE, FAKE, accept_len, None)
+
+    assert call(logits=None) == E
+    assert call(pred=None) == E
+    assert call(accept_len=FAKE + 2) == E
+    assert call(v=None) == E
+    assert call(V=0) == E
+    assert call(ckv=FAKE) == E                        # one cache without the other
+    assert call(ckv=FAKE + 8, k_rope=FAKE) == E       # misaligned cache
+    assert call(ckv=FAKE, k_rope=FAKE, dtype=5) == U
 
 
 def test_plan_rules(lib):

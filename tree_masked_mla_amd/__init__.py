@@ -27,7 +27,7 @@ D_LATENT, D_ROPE, MAX_Q = 512, 64, 256
 EXPORTED = (
     "ddtv_vis_bytes", "ddtv_build_visibility", "ddtv_read_status", "ddtv_workspace_bytes",
     "ddtv_workspace_bytes_ex", "ddtv_verify_attn", "ddtv_verify_attn_ex", "ddtv_plan_info",
-    "ddtv_status_string", "ddtv_version", "ddtv_build_tree",
+    "ddtv_status_string", "ddtv_version", "ddtv_build_tree", "ddtv_tree_accept",
 )
 
 
@@ -85,6 +85,8 @@ def load(path: str = LIB_PATH):
     lib.ddtv_plan_info.restype = ctypes.c_int
     lib.ddtv_build_tree.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P, P]
     lib.ddtv_build_tree.restype = ctypes.c_int
+    lib.ddtv_tree_accept.argtypes = [P, i32, P, P, VP, P, P, ctypes.c_int, P, P, P, P, P]
+    lib.ddtv_tree_accept.restype = ctypes.c_int
     lib.ddtv_status_string.argtypes = [ctypes.c_int]
     lib.ddtv_status_string.restype = ctypes.c_char_p
     lib.ddtv_version.argtypes = []
@@ -195,6 +197,15 @@ def ddtv_build_tree(logp, Q: int, parent, tokens=None, depth=None, rank=None, to
     B, D, K = (int(x) for x in logp.shape)
     return load().ddtv_build_tree(_ptr(logp), _ptr(tokens), B, D, K, Q, _ptr(parent), _ptr(depth), _ptr(rank),
                                   _ptr(token), _ptr(score), _stream(stream))
+
+
+def ddtv_tree_accept(logits, parent, token, vis: Visibility, pred, path, out_tokens, accept_len, ckv=None,
+                     k_rope=None, kv_dtype: int = DDTV_F32, stream=None) -> int:
+    """logits: device float32 [B][Q][V]; parent/token: device int32 [B][Q]; outputs: device int32 tensors."""
+    V = int(logits.shape[-1])
+    return load().ddtv_tree_accept(_ptr(logits), V, _ptr(parent), _ptr(token), ctypes.byref(vis.vis), _ptr(ckv),
+                                   _ptr(k_rope), kv_dtype, _ptr(pred), _ptr(path), _ptr(out_tokens),
+                                   _ptr(accept_len), _stream(stream))
 
 
 def ddtv_verify_attn(q_abs, q_rope, ckv, k_rope, kv_dtype: int, H: int, vis: Visibility, scale: float, out,

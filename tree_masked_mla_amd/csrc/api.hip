@@ -17,7 +17,7 @@ using namespace ddtv;
 
 namespace {
 
-constexpr int32_t kVersion = 400;   // 0.4.0: best-first draft-tree builder
+constexpr int32_t kVersion = 500;   // 0.5.0: greedy tree acceptance and cache compaction
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -401,6 +401,40 @@ ddtv_status ddtv_build_tree(const float* logp, const int32_t* tokens, int32_t B,
     a.K = K;
     a.Q = Q;
     return launch_tree_build(a, stream) == hipSuccess ? DDTV_OK : DDTV_EDEVICE;
+}
+
+ddtv_status ddtv_tree_accept(const float* logits, int32_t V, const int32_t* parent, const int32_t* token,
+                             const ddtv_vis* vis, void* ckv, void* k_rope, ddtv_dtype kv_dtype, int32_t* pred,
+                             int32_t* path, int32_t* out_tokens, int32_t* accept_len, hipStream_t stream) {
+    if (!logits || !parent || !token || !pred || !path || !out_tokens || !accept_len) return DDTV_EINVAL;
+    if (!aligned(logits, 4) || !aligned(parent, 4) || !aligned(token, 4) || !aligned(pred, 4) ||
+        !aligned(path, 4) || !aligned(out_tokens, 4) || !aligned(accept_len, 4))
+        return DDTV_EINVAL;
+    ddtv_status st = check_vis(vis);
+    if (st) return st;
+    if (V < 1) return DDTV_EINVAL;
+    if ((ckv == nullptr) != (k_rope == nullptr)) return DDTV_EINVAL;
+    if (ckv) {
+        if (!aligned(ckv, 16) || !aligned(k_rope, 16)) return DDTV_EINVAL;
+        if (kv_dtype != DDTV_F32 && kv_dtype != DDTV_BF16) return DDTV_EUNSUPPORTED;
+    }
+    if ((int64_t)vis->B * vis->Q > (int64_t)UINT32_MAX) return DDTV_EUNSUPPORTED;
+    AcceptArgs a;
+    a.logits = logits;
+    a.parent = parent;
+    a.token = token;
+    a.rows = vis->rows;
+    a.pred = pred;
+    a.path = path;
+    a.out_tokens = out_tokens;
+    a.accept_len = accept_len;
+    a.ckv = ckv;
+    a.k_rope = k_rope;
+    a.kv_elem = kv_dtype == DDTV_BF16 ? 2 : 4;
+    a.B = vis->B;
+    a.Q = vis->Q;
+    a.V = V;
+    return launch_tree_accept(a, stream) == hipSuccess ? DDTV_OK : DDTV_EDEVICE;
 }
 
 ddtv_status ddtv_read_status(const ddtv_vis* vis, int32_t* bad_row, int32_t* bad_node, hipStream_t stream) {

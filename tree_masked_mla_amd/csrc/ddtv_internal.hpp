@@ -53,6 +53,22 @@ struct TreeArgs {
 };
 constexpr int kMaxTreeK = 64;   // choices per depth the builder accepts
 
+// Everything the tree-accept step needs (passed by value).
+struct AcceptArgs {
+    const float* logits;     // [B][Q][V]
+    const int32_t* parent;   // [B][Q]
+    const int32_t* token;    // [B][Q] draft tokens
+    const ddtv_row* rows;    // [B] cache geometry (compaction)
+    int32_t* pred;           // [B][Q] out
+    int32_t* path;           // [B][Q] out
+    int32_t* out_tokens;     // [B][Q] out
+    int32_t* accept_len;     // [B] out
+    void* ckv;               // [total_kv][512] or null: no compaction
+    void* k_rope;            // [total_kv][64]
+    int kv_elem;             // bytes per cache element (4 or 2)
+    int B, Q, V;
+};
+
 struct VisChunk {
     int64_t kv_off[kVisChunk];
     int32_t prefix[kVisChunk];
@@ -70,6 +86,7 @@ hipError_t launch_attn_mfma_bf16(const AttnArgs& a, int64_t grid, hipStream_t st
 int bf16_rows_per_workgroup();   // query rows per workgroup of the bf16 MFMA kernel
 hipError_t launch_merge(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_tree_build(const TreeArgs& a, hipStream_t stream);
+hipError_t launch_tree_accept(const AcceptArgs& a, hipStream_t stream);
 
 constexpr int kValuRows = 16;   // query rows per VALU workgroup
 
