@@ -148,6 +148,37 @@ def time_tree_builder(dd, hip, stream, dev, B, Q, D=12, K=4, steps=20, warmup=3)
             "note": "one wave per tree, one node per step: bound by the dependent chain of Q steps"}
 
 
+def time_tree_accept(dd, hip, stream, r, V=32768, steps=20, warmup=3):
+    """The accept step (ddtv_tree_accept) on the benchmarked trees: target argmax over
+    V synthetic logits per node, the greedy walk and in-place compaction of the
+    accepted rows of the resident caches; average launch time from HIP events."""
+    import torch
+    import workloads as wl
+    B, Q = r.B, r.Q
+    dev = r.device
+    logits = torch.from_numpy(wl.target_logits(7100 + B + Q, B, Q, V)).to(dev)
+    tok = torch.from_numpy(np.ascontiguousarray(r.w.parent % 997, dtype=np.int32)).to(dev)   # any draft tokens
+    o = [torch.empty((B, Q), dtype=torch.int32, device=dev) for _ in range(3)]
+    alen = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def launch():
+        rc = dd.ddtv_tree_accept(logits, r.parent, tok, r.vis, o[0], o[1], o[2], alen, ckv=r.ckv, k_rope=r.k_rope,
+                                 kv_dtype=r.kv_dtype, stream=stream)
+        assert rc == dd.DDTV_OK, rc
+    for _ in range(warmup):
+        launch()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for _ in range(steps):
+        launch()
+    hip.record(e1, stream)
+    us = hip.elapsed_ms(e0, e1) * 1e3 / steps
+    logit_bytes = B * Q * V * 4
+    return {"workload": f"B={B} trees of Q={Q} nodes, V={V} synthetic target logits per node, compaction on",
+            "us_per_launch": round(us, 2), "logit_bytes": logit_bytes,
+            "logits_gbps": round(logit_bytes / (us * 1e-6) / 1e9, 1), "launches": steps}
+
+
 def cpu_baseline(w, budget_s=15.0, max_rows=4096):
     """The oracle (single-threaded fp64 C) on a seeded sample of query rows of the
     same workload, for about budget_s seconds.  Reported as tree-query tokens/s
@@ -298,6 +329,7 @@ def main():
         },
     }
     out["tree_build"] = time_tree_builder(dd, hip, stream, dev, w.B, w.Q)
+    out["tree_accept"] = time_tree_accept(dd, hip, stream, r)
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(w, budget_s=args.cpu_budget)

@@ -50,6 +50,28 @@ def test_accept_matches_oracle(seed, B, Q, V):
     assert ref["accept_len"].max() >= 1
 
 
+def test_accept_unaligned_logits():
+    """Logits that start 4 bytes past a 16-byte boundary take the scalar path."""
+    import tree_masked_mla_amd as dd
+    parent, token, logits = random_case(12, 3, 24, V=64)
+    rc, ref = oracle.tree_accept(logits, parent, token)
+    dev = torch.device("cuda:0")
+    B, Q, V = logits.shape
+    flat = torch.zeros(B * Q * V + 4, dtype=torch.float32, device=dev)
+    flat[1:1 + B * Q * V] = torch.from_numpy(logits.reshape(-1)).to(dev)
+    lg = flat[1:1 + B * Q * V].view(B, Q, V)
+    assert lg.data_ptr() % 16 == 4
+    par_d = torch.from_numpy(parent).to(dev)
+    buf = torch.empty(dd.ddtv_vis_bytes(B, Q), dtype=torch.uint8, device=dev)
+    rc, vis = dd.ddtv_build_visibility(par_d, np.zeros(B, np.int32), B, Q, buf)
+    o = [torch.empty((B, Q), dtype=torch.int32, device=dev) for _ in range(3)]
+    alen = torch.empty(B, dtype=torch.int32, device=dev)
+    assert dd.ddtv_tree_accept(lg, par_d, torch.from_numpy(token).to(dev), vis, o[0], o[1], o[2], alen) == dd.DDTV_OK
+    torch.cuda.synchronize()
+    assert np.array_equal(o[0].cpu().numpy(), ref["pred"])
+    assert np.array_equal(alen.cpu().numpy(), ref["accept_len"])
+
+
 def test_accept_ties_in_logits():
     parent, token, logits = random_case(11, 3, 40, V=64)
     logits = np.round(logits)                     # many equal maxima: the lowest index wins

@@ -17,9 +17,9 @@
 // Three launches on the caller's stream:
 //  * accept_argmax_kernel: one 256-thread workgroup per (batch row, node); each
 //    thread keeps the first maximum of its strided share of the V logits
-//    (coalesced), then a workgroup reduction keeps the larger value, and on equal
-//    values the lower index.  This part reads B*Q*V floats and is HBM-bound for
-//    a real vocabulary.
+//    (coalesced, 16-byte loads four at a time when V is a multiple of 4), then a
+//    workgroup reduction keeps the larger value, and on equal values the lower
+//    index.  This part reads B*Q*V floats and is HBM-bound for a real vocabulary.
 //  * accept_walk_kernel: one wave per batch row; at each step all lanes test the
 //    candidate children in parallel (64 node indices per ballot) and the lowest
 //    matching index is taken.
@@ -46,12 +46,40 @@ __global__ __launch_bounds__(kArgmaxThreads) void accept_argmax_kernel(const flo
     const int t = threadIdx.x;
     float best = -INFINITY;
     int bi = -1;
-    for (int v = t; v < V; v += kArgmaxThreads) {
-        const float y = x[v];
+    auto take = [&](float y, int v) {   // first maximum in the order visited
         if (bi < 0 || y > best) {
             best = y;
             bi = v;
         }
+    };
+    if ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0) {
+        // 16-byte loads (rows start 16-byte aligned), four in flight per thread; a thread visits its chunks in
+        // increasing order and each chunk's elements in order
+        const float4* x4 = reinterpret_cast<const float4*>(x);
+        const int n4 = V >> 2;
+        int c = t;
+        for (; c + 3 * kArgmaxThreads < n4; c += 4 * kArgmaxThreads) {
+            float4 q[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) q[u] = x4[c + u * kArgmaxThreads];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int v = 4 * (c + u * kArgmaxThreads);
+                take(q[u].x, v);
+                take(q[u].y, v + 1);
+                take(q[u].z, v + 2);
+                take(q[u].w, v + 3);
+            }
+        }
+        for (; c < n4; c += kArgmaxThreads) {
+            const float4 q = x4[c];
+            take(q.x, 4 * c);
+            take(q.y, 4 * c + 1);
+            take(q.z, 4 * c + 2);
+            take(q.w, 4 * c + 3);
+        }
+    } else {
+        for (int v = t; v < V; v += kArgmaxThreads) take(x[v], v);
     }
     sv[t] = best;
     si[t] = bi;

@@ -272,6 +272,11 @@ def drafter_topk(seed: int, B: int, D: int, K: int, vocab: int = 32, sigma: floa
             np.ascontiguousarray(order, dtype=np.int32))
 
 
+def target_logits(seed: int, B: int, Q: int, V: int) -> np.ndarray:
+    """Synthetic target-model logits after each tree node: float32 [B][Q][V], N(0, 1)."""
+    return np.random.default_rng(seed).standard_normal((B, Q, V), dtype=np.float32)
+
+
 def sample_rows(w: Workload, n: int, seed: int = 7) -> np.ndarray:
     """Seeded sample of n flat query-row ids (b*Q + q)*H + h spread over all batch rows."""
     rng = np.random.default_rng(seed)
