@@ -252,6 +252,33 @@ ddtv_status ddtv_verify_attn_ex(const float *q_abs, const float *q_rope, const v
                                 void *workspace, size_t workspace_bytes, hipStream_t stream,
                                 const ddtv_opts *opts);
 
+/*
+ * External-prefix mode: the caller brings each query row's attention over the
+ * shared prefix (from any prefix kernel); this call attends only the tree rows
+ * and merges the two by log-sum-exp.
+ *   Pages: "The Verify-Attn Kernel: A Single File Write ...", section "Design
+ *   Decisions and Trade-Offs" (a prefix kernel for the long prefix, the masked
+ *   kernel for the tree tail, merged by log-sum-exp).
+ *   prefix_out  DEVICE float [B][Q][H][512], 16-byte aligned: softmax-weighted
+ *               latent over the prefix rows only (normalised)
+ *   prefix_lse  DEVICE float [B][Q][H]: its natural-log log-sum-exp; -inf for a
+ *               batch row without prefix (prefix_out is then ignored)
+ *   other arguments as for ddtv_verify_attn_ex; out/lse receive the merged result,
+ *   which equals ddtv_verify_attn over prefix and tree when the prefix result is
+ *   exact.  workspace: at least ddtv_tail_workspace_bytes(), 256-byte aligned
+ *   (never NULL: it also holds a row table and the tree rows' lse).
+ * Errors: as ddtv_verify_attn_ex, plus DDTV_EINVAL for a null or misaligned prefix
+ * result.
+ */
+size_t ddtv_tail_workspace_bytes(const ddtv_vis *vis, int32_t H, ddtv_dtype kv_dtype,
+                                 const ddtv_opts *opts);
+ddtv_status ddtv_verify_attn_tail(const float *q_abs, const float *q_rope, const void *ckv,
+                                  const void *k_rope, ddtv_dtype kv_dtype, int32_t H,
+                                  const ddtv_vis *vis, float scale, const float *prefix_out,
+                                  const float *prefix_lse, float *out, float *lse,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                  const ddtv_opts *opts);
+
 /* Describes the plan ddtv_verify_attn_ex would run (HOST out params, may be NULL):
  * path taken, KV positions per split, maximum splits per batch row, workgroups
  * of the main kernel, workgroup order (DDTV_ORDER_XCD_LOCAL or DDTV_ORDER_SPREAD).

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert dd.ddtv_version() == 500
+    assert dd.ddtv_version() == 600
     for code in range(6):
         assert dd.ddtv_status_string(code)
     assert dd.ddtv_status_string(2).startswith("malformed tree")
@@ -175,6 +175,24 @@ def test_tree_accept_argument_checks(lib):
     assert call(ckv=FAKE) == E                        # one cache without the other
     assert call(ckv=FAKE + 8, k_rope=FAKE) == E       # misaligned cache
     assert call(ckv=FAKE, k_rope=FAKE, dtype=5) == U
+
+
+def test_tail_mode_argument_checks(lib):
+    """The external-prefix call's host checks come before any HIP call."""
+    vis = fake_vis(B=2, Q=24, prefix=(100, 0))
+    need = dd.ddtv_tail_workspace_bytes(vis, 8, 0)
+    assert need >= 2 * 16 + 2 * 24 * 8 * 4
+
+    def call(po=FAKE, pl=FAKE, ws=FAKE, ws_bytes=need):
+        return lib.ddtv_verify_attn_tail(FAKE, FAKE, FAKE, FAKE, 0, 8, ctypes.byref(vis.vis), ctypes.c_float(0.07),
+                                         po, pl, FAKE, None, ws, ws_bytes, None, None)
+
+    assert call(po=None) == dd.DDTV_EINVAL
+    assert call(pl=None) == dd.DDTV_EINVAL
+    assert call(po=FAKE + 4) == dd.DDTV_EINVAL            # prefix output must be 16-byte aligned
+    assert call(ws=None) == dd.DDTV_EWORKSPACE
+    assert call(ws_bytes=need - 1) == dd.DDTV_EWORKSPACE
+    assert call(ws=FAKE + 16) == dd.DDTV_EINVAL           # workspace must be 256-byte aligned
 
 
 def test_plan_rules(lib):

@@ -28,6 +28,7 @@ EXPORTED = (
     "ddtv_vis_bytes", "ddtv_build_visibility", "ddtv_read_status", "ddtv_workspace_bytes",
     "ddtv_workspace_bytes_ex", "ddtv_verify_attn", "ddtv_verify_attn_ex", "ddtv_plan_info",
     "ddtv_status_string", "ddtv_version", "ddtv_build_tree", "ddtv_tree_accept",
+    "ddtv_tail_workspace_bytes", "ddtv_verify_attn_tail",
 )
 
 
@@ -87,6 +88,10 @@ def load(path: str = LIB_PATH):
     lib.ddtv_build_tree.restype = ctypes.c_int
     lib.ddtv_tree_accept.argtypes = [P, i32, P, P, VP, P, P, ctypes.c_int, P, P, P, P, P]
     lib.ddtv_tree_accept.restype = ctypes.c_int
+    lib.ddtv_tail_workspace_bytes.argtypes = [VP, i32, ctypes.c_int, OP]
+    lib.ddtv_tail_workspace_bytes.restype = sz
+    lib.ddtv_verify_attn_tail.argtypes = [P, P, P, P, ctypes.c_int, i32, VP, ctypes.c_float, P, P, P, P, P, sz, P, OP]
+    lib.ddtv_verify_attn_tail.restype = ctypes.c_int
     lib.ddtv_status_string.argtypes = [ctypes.c_int]
     lib.ddtv_status_string.restype = ctypes.c_char_p
     lib.ddtv_version.argtypes = []
@@ -206,6 +211,22 @@ def ddtv_tree_accept(logits, parent, token, vis: Visibility, pred, path, out_tok
     return load().ddtv_tree_accept(_ptr(logits), V, _ptr(parent), _ptr(token), ctypes.byref(vis.vis), _ptr(ckv),
                                    _ptr(k_rope), kv_dtype, _ptr(pred), _ptr(path), _ptr(out_tokens),
                                    _ptr(accept_len), _stream(stream))
+
+
+def ddtv_tail_workspace_bytes(vis: Visibility, H: int, kv_dtype: int, opts: ddtv_opts | None = None) -> int:
+    return load().ddtv_tail_workspace_bytes(ctypes.byref(vis.vis), H, kv_dtype,
+                                            ctypes.byref(opts) if opts is not None else None)
+
+
+def ddtv_verify_attn_tail(q_abs, q_rope, ckv, k_rope, kv_dtype: int, H: int, vis: Visibility, scale: float,
+                          prefix_out, prefix_lse, out, lse, workspace, workspace_bytes: int | None = None,
+                          stream=None, opts: ddtv_opts | None = None) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return load().ddtv_verify_attn_tail(_ptr(q_abs), _ptr(q_rope), _ptr(ckv), _ptr(k_rope), kv_dtype, H,
+                                        ctypes.byref(vis.vis), ctypes.c_float(scale), _ptr(prefix_out),
+                                        _ptr(prefix_lse), _ptr(out), _ptr(lse), _ptr(workspace), workspace_bytes,
+                                        _stream(stream), ctypes.byref(opts) if opts is not None else None)
 
 
 def ddtv_verify_attn(q_abs, q_rope, ckv, k_rope, kv_dtype: int, H: int, vis: Visibility, scale: float, out,

@@ -12,12 +12,13 @@
 #include <vector>
 
 #include "ddtv_internal.hpp"
+#include "tail.hpp"
 
 using namespace ddtv;
 
 namespace {
 
-constexpr int32_t kVersion = 500;   // 0.5.0: greedy tree acceptance and cache compaction
+constexpr int32_t kVersion = 600;   // 0.6.0: external-prefix (tree-tail) mode
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -301,6 +302,39 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     return DDTV_OK;
 }
 
+// External-prefix (tree-tail) mode: the same trees seen without their prefix --
+// each batch row's Q tree rows as a row of its own -- over a row table that a
+// small kernel writes into the workspace.  Workspace: that table, the tree
+// rows' lse, then the tail plan's own workspace.
+struct TailLayout {
+    size_t rows = 0, lse = 0, plan = 0, total = 0;
+};
+
+ddtv_vis tail_view(const ddtv_vis* vis, ddtv_row* rows) {
+    ddtv_vis t = *vis;
+    t.rows = rows;
+    t.order = nullptr;
+    t.prefix_host = nullptr;
+    t.max_kv = vis->Q;
+    t.total_kv = (int64_t)vis->B * vis->Q;
+    return t;
+}
+
+ddtv_status tail_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const ddtv_opts* opts, TailLayout* L,
+                      Plan* p) {
+    ddtv_status st = check_vis(vis);
+    if (st) return st;
+    if (H < 1 || H > 65536) return DDTV_EINVAL;
+    const ddtv_vis t = tail_view(vis, vis->rows);   // geometry only: planning reads no device data
+    st = make_plan(&t, H, kv_dtype, opts, p);
+    if (st) return st;
+    L->rows = 0;
+    L->lse = round_up((size_t)vis->B * sizeof(ddtv_row), 256);
+    L->plan = L->lse + round_up((size_t)vis->B * vis->Q * (size_t)H * sizeof(float), 256);
+    L->total = L->plan + p->ws_bytes;
+    return DDTV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -401,6 +435,37 @@ ddtv_status ddtv_build_tree(const float* logp, const int32_t* tokens, int32_t B,
     a.K = K;
     a.Q = Q;
     return launch_tree_build(a, stream) == hipSuccess ? DDTV_OK : DDTV_EDEVICE;
+}
+
+size_t ddtv_tail_workspace_bytes(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const ddtv_opts* opts) {
+    TailLayout L;
+    Plan p;
+    return tail_plan(vis, H, kv_dtype, opts, &L, &p) == DDTV_OK ? L.total : 0;
+}
+
+ddtv_status ddtv_verify_attn_tail(const float* q_abs, const float* q_rope, const void* ckv, const void* k_rope,
+                                  ddtv_dtype kv_dtype, int32_t H, const ddtv_vis* vis, float scale,
+                                  const float* prefix_out, const float* prefix_lse, float* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream, const ddtv_opts* opts) {
+    if (!prefix_out || !prefix_lse || !out) return DDTV_EINVAL;
+    if (!aligned(prefix_out, 16) || !aligned(prefix_lse, 4)) return DDTV_EINVAL;
+    TailLayout L;
+    Plan p;
+    ddtv_status st = tail_plan(vis, H, kv_dtype, opts, &L, &p);
+    if (st) return st;
+    if (!workspace || workspace_bytes < L.total) return DDTV_EWORKSPACE;
+    if (!aligned(workspace, 256)) return DDTV_EINVAL;
+    char* ws = static_cast<char*>(workspace);
+    ddtv_row* rows = reinterpret_cast<ddtv_row*>(ws + L.rows);
+    float* lse_tail = reinterpret_cast<float*>(ws + L.lse);
+    const ddtv_vis t = tail_view(vis, rows);
+    if (launch_tail_rows(vis->rows, rows, vis->B, vis->Q, stream) != hipSuccess) return DDTV_EDEVICE;
+    st = ddtv_verify_attn_ex(q_abs, q_rope, ckv, k_rope, kv_dtype, H, &t, scale, out, lse_tail, ws + L.plan,
+                             workspace_bytes - L.plan, stream, opts);
+    if (st) return st;
+    const int64_t n = (int64_t)vis->B * vis->Q * H;
+    return launch_tail_merge(out, lse_tail, lse, prefix_out, prefix_lse, n, stream) == hipSuccess ? DDTV_OK
+                                                                                                     : DDTV_EDEVICE;
 }
 
 ddtv_status ddtv_tree_accept(const float* logits, int32_t V, const int32_t* parent, const int32_t* token,
