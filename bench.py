@@ -179,6 +179,33 @@ def time_tree_accept(dd, hip, stream, r, V=32768, steps=20, warmup=3):
             "logits_gbps": round(logit_bytes / (us * 1e-6) / 1e9, 1), "launches": steps}
 
 
+def time_tail_mode(dd, hip, stream, r, steps=20, warmup=3):
+    """External-prefix mode on the benchmarked workload: the tree rows only, merged
+    with a prefix result supplied by the caller (here any normalised rows and
+    finite lse: timing only); average call time from HIP events."""
+    import torch
+    w = r.w
+    po = torch.zeros_like(r.out)
+    pl = torch.zeros((w.B, w.Q, w.H), dtype=torch.float32, device=r.device)
+    need = dd.ddtv_tail_workspace_bytes(r.vis, w.H, w.kv_dtype)
+    ws = torch.empty(need, dtype=torch.uint8, device=r.device)
+
+    def launch():
+        rc = dd.ddtv_verify_attn_tail(r.q_abs, r.q_rope, r.ckv, r.k_rope, w.kv_dtype, w.H, r.vis, w.scale, po, pl,
+                                      r.out, r.lse, ws, stream=stream)
+        assert rc == dd.DDTV_OK, rc
+    for _ in range(warmup):
+        launch()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for _ in range(steps):
+        launch()
+    hip.record(e1, stream)
+    us = hip.elapsed_ms(e0, e1) * 1e3 / steps
+    return {"workload": f"the same trees, tree rows only ({w.Q} per batch row) + merge with a caller's prefix result",
+            "us_per_call": round(us, 2), "calls": steps}
+
+
 def cpu_baseline(w, budget_s=15.0, max_rows=4096):
     """The oracle (single-threaded fp64 C) on a seeded sample of query rows of the
     same workload, for about budget_s seconds.  Reported as tree-query tokens/s
@@ -329,6 +356,7 @@ def main():
         },
     }
     out["tree_build"] = time_tree_builder(dd, hip, stream, dev, w.B, w.Q)
+    out["tail_mode"] = time_tail_mode(dd, hip, stream, r)
     out["tree_accept"] = time_tree_accept(dd, hip, stream, r)
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
