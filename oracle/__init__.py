@@ -6,7 +6,9 @@ arithmetic lives in ``ddtv_oracle.c`` (plain fp64 C, single-threaded); this file
 only compiles it with gcc, marshals numpy arrays and returns numpy results.
 The best-first draft-tree builder's oracle lives in ``ddtv_tree_oracle.c``
 (plain C, a binary heap) and the greedy tree-accept step's in
-``ddtv_accept_oracle.c``, compiled into the same library.
+``ddtv_accept_oracle.c``, and the steps around the attention (query split with
+rotary embedding and absorb, value projection, appended key rows) in
+``ddtv_neighbour_oracle.c``, all compiled into the same library.
 """
 from __future__ import annotations
 
@@ -20,7 +22,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ddtv_oracle.c")
 _SRC_TREE = os.path.join(_HERE, "ddtv_tree_oracle.c")
 _SRC_ACCEPT = os.path.join(_HERE, "ddtv_accept_oracle.c")
-SOURCES = (_SRC, _SRC_TREE, _SRC_ACCEPT)
+_SRC_NEIGHBOUR = os.path.join(_HERE, "ddtv_neighbour_oracle.c")
+SOURCES = (_SRC, _SRC_TREE, _SRC_ACCEPT, _SRC_NEIGHBOUR)
 _LIB = os.path.join(_HERE, "libddtv_oracle.so")
 
 REF_OK, REF_EINVAL, REF_ETREE = 0, 1, 2
@@ -57,6 +60,15 @@ def configure(lib):
     lib.ddtvref_tree_accept_row.restype = ctypes.c_int
     lib.ddtvref_compact_rows.argtypes = [P, P, i64, i64, i32, P, i32]
     lib.ddtvref_compact_rows.restype = None
+    lib.ddtvref_rope_neox.argtypes = [P, i32, f64, P]
+    lib.ddtvref_rope_neox.restype = None
+    lib.ddtvref_tree_positions.argtypes = [P, P, i32, i32, P]
+    lib.ddtvref_prepare_query.argtypes = [P, i32, i32, i32, P, f64, P, P, P]
+    lib.ddtvref_value_proj.argtypes = [P, i32, i32, i32, P, P]
+    lib.ddtvref_append_kv.argtypes = [P, P, P, P, i32, i32, f64, P, P]
+    for name in ("ddtvref_tree_positions", "ddtvref_prepare_query", "ddtvref_value_proj",
+                 "ddtvref_append_kv"):
+        getattr(lib, name).restype = ctypes.c_int
     for name in ("ddtvref_build_visibility", "ddtvref_verify_attn_rows",
                  "ddtvref_row_probs", "ddtvref_partial", "ddtvref_merge", "ddtvref_words"):
         getattr(lib, name).restype = ctypes.c_int
@@ -235,3 +247,75 @@ def compact_rows(rows: np.ndarray, prefix: int, path: np.ndarray, k: int) -> np.
     _load().ddtvref_compact_rows(_p(src.view(np.uint8)), _p(dst.view(np.uint8)), n, row_bytes, prefix,
                                  _p(_c(path, np.int32)), k)
     return dst
+
+
+def rope_neox(x: np.ndarray, pos: int, theta: float) -> np.ndarray:
+    """NeoX rotation of one 64-wide float32 vector at position ``pos`` (float64 out)."""
+    x = _c(x, np.float32).reshape(D_ROPE)
+    y = np.zeros(D_ROPE, dtype=np.float64)
+    _load().ddtvref_rope_neox(_p(x), int(pos), float(theta), _p(y))
+    return y
+
+
+def tree_positions(parent: np.ndarray, prefix: np.ndarray) -> np.ndarray:
+    """Position of every tree node: prefix[b] + depth (int32 [B][Q])."""
+    parent = _c(parent, np.int32)
+    B, Q = parent.shape
+    pos = np.zeros((B, Q), dtype=np.int32)
+    rc = _load().ddtvref_tree_positions(_p(parent), _p(_c(prefix, np.int32)), B, Q, _p(pos))
+    if rc != REF_OK:
+        raise ValueError(f"oracle tree_positions failed with code {rc}")
+    return pos
+
+
+def prepare_query(q: np.ndarray, pos: np.ndarray, theta: float, w_kc: np.ndarray):
+    """q float32 [..., H, d_nope + 64] (leading dims = tokens), pos int32 [tokens],
+    w_kc float32 [H][d_nope][512] -> (q_abs float64 [..., H, 512], q_rope float64 [..., H, 64])."""
+    q = _c(q, np.float32)
+    lead = q.shape[:-2]
+    H, row = q.shape[-2], q.shape[-1]
+    d_nope = row - D_ROPE
+    M = int(np.prod(lead)) if lead else 1
+    w_kc = _c(w_kc, np.float32)
+    assert w_kc.shape == (H, d_nope, D_LATENT)
+    pos = _c(pos, np.int32).reshape(-1)
+    assert pos.shape[0] == M
+    q_abs = np.zeros(lead + (H, D_LATENT), dtype=np.float64)
+    q_rope = np.zeros(lead + (H, D_ROPE), dtype=np.float64)
+    rc = _load().ddtvref_prepare_query(_p(q), M, H, d_nope, _p(pos), float(theta), _p(w_kc),
+                                       _p(q_abs), _p(q_rope))
+    if rc != REF_OK:
+        raise ValueError(f"oracle prepare_query failed with code {rc}")
+    return q_abs, q_rope
+
+
+def value_proj(o: np.ndarray, w_vc: np.ndarray) -> np.ndarray:
+    """o float32 [..., H, 512], w_vc float32 [H][d_v][512] -> v float64 [..., H, d_v]."""
+    o = _c(o, np.float32)
+    lead = o.shape[:-2]
+    H = o.shape[-2]
+    M = int(np.prod(lead)) if lead else 1
+    w_vc = _c(w_vc, np.float32)
+    assert w_vc.shape[0] == H and w_vc.shape[2] == D_LATENT
+    d_v = w_vc.shape[1]
+    v = np.zeros(lead + (H, d_v), dtype=np.float64)
+    rc = _load().ddtvref_value_proj(_p(o), M, H, d_v, _p(w_vc), _p(v))
+    if rc != REF_OK:
+        raise ValueError(f"oracle value_proj failed with code {rc}")
+    return v
+
+
+def append_kv(latent, k_pe, pos, prefix, theta, ckv, k_rope):
+    """Write B trees' new cache rows into float64 copies of ckv [total][512] and
+    k_rope [total][64]; latent float32 [B][Q][512], k_pe float32 [B][Q][64],
+    pos int32 [B][Q].  Returns the two new arrays."""
+    latent = _c(latent, np.float32)
+    k_pe = _c(k_pe, np.float32)
+    B, Q, _ = latent.shape
+    ckv = np.array(ckv, dtype=np.float64, copy=True, order="C")
+    k_rope = np.array(k_rope, dtype=np.float64, copy=True, order="C")
+    rc = _load().ddtvref_append_kv(_p(latent), _p(k_pe), _p(_c(pos, np.int32)), _p(_c(prefix, np.int32)),
+                                   B, Q, float(theta), _p(ckv), _p(k_rope))
+    if rc != REF_OK:
+        raise ValueError(f"oracle append_kv failed with code {rc}")
+    return ckv, k_rope

@@ -17,10 +17,15 @@ import oracle
 import test_oracle_pins as pins
 import test_accept_oracle as accept_pins
 import test_tree_oracle as tree_pins
+import test_neighbour_oracle as nb_pins
+import workloads
+
+wl_theta = workloads.ROPE_THETA
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ddtv_oracle.c")
 SRC_TREE = os.path.join(os.path.dirname(oracle.__file__), "ddtv_tree_oracle.c")
 SRC_ACCEPT = os.path.join(os.path.dirname(oracle.__file__), "ddtv_accept_oracle.c")
+SRC_NEIGHBOUR = os.path.join(os.path.dirname(oracle.__file__), "ddtv_neighbour_oracle.c")
 
 # (id, original text, mutated text)
 MUTATIONS = [
@@ -98,6 +103,37 @@ ACCEPT_PINS = [
     lambda: accept_pins.test_compaction_equals_fancy_indexing(np.float32),
 ]
 
+# Mistakes planted in the oracle of the steps around the attention.
+NEIGHBOUR_MUTATIONS = [
+    ("rope_interleaved_pairs", "double x0 = (double)x[i], x1 = (double)x[i + N_HALF];",
+     "double x0 = (double)x[2 * i], x1 = (double)x[2 * i + 1];"),
+    ("rope_sign", "y[i] = x0 * c - x1 * s;", "y[i] = x0 * c + x1 * s;"),
+    ("rope_frequency_exponent", "-(double)(2 * i) / (double)N_ROPE", "-(double)(i) / (double)N_ROPE"),
+    ("rope_reads_nope_part", "const float *pe = nope + d_nope;", "const float *pe = nope;"),
+    ("absorb_head_and_row_swapped", "w_kc[(h * d_nope + k) * N_LAT + c]", "w_kc[(k * H + h) * N_LAT + c]"),
+    ("absorb_drops_last_term", "for (int k = 0; k < d_nope; ++k)", "for (int k = 0; k < d_nope - 1; ++k)"),
+    ("value_wrong_head", "const float *w = w_vc + (h * d_v + n) * N_LAT;",
+     "const float *w = w_vc + (((h + 1) % H) * d_v + n) * N_LAT;"),
+    ("value_column_shift", "acc += (double)x[c] * (double)w[c];", "acc += (double)x[c] * (double)w[c ^ 1];"),
+    ("position_ignores_prefix", "pos[(int64_t)b * Q + i] = prefix[b] + d;", "pos[(int64_t)b * Q + i] = d;"),
+    ("position_counts_root", "int32_t d = 0;", "int32_t d = 1;"),
+    ("append_key_unrotated", "ddtvref_rope_neox(k_pe + node * N_ROPE, pos[node], theta, k_rope + r * N_ROPE);",
+     "ddtvref_rope_neox(k_pe + node * N_ROPE, 0, theta, k_rope + r * N_ROPE);"),
+    ("append_row_ignores_prefix", "int64_t r = off + prefix[b] + i;", "int64_t r = off + i;"),
+]
+
+NEIGHBOUR_PINS = [
+    lambda: nb_pins.test_rope_is_complex_rotation(wl_theta),
+    nb_pins.test_rope_unit_vectors_closed_form,
+    nb_pins.test_rope_identity_norms_and_relative_positions,
+    nb_pins.test_absorb_equals_unabsorbed_key_and_rope_part,
+    nb_pins.test_absorb_one_hot_picks_weight_rows,
+    nb_pins.test_value_projection_matmul_and_one_hot,
+    nb_pins.test_tree_positions,
+    nb_pins.test_append_kv_rows,
+    lambda: nb_pins.test_chain_equals_unabsorbed_attention(128, 128),
+]
+
 TREE_PINS = [
     lambda: tree_pins.test_bruteforce_top_scores(3, 3, 20),
     lambda: tree_pins.test_bruteforce_top_scores(5, 3, 60),
@@ -116,7 +152,7 @@ def _run_mutation(tmp_path, target, mid, old, new, pins_to_run):
     c = tmp_path / ("mut_" + os.path.basename(target))
     so = tmp_path / "libmut.so"
     c.write_text(mutated)
-    sources = [str(c) if f == target else f for f in (SRC, SRC_TREE, SRC_ACCEPT)]
+    sources = [str(c) if f == target else f for f in (SRC, SRC_TREE, SRC_ACCEPT, SRC_NEIGHBOUR)]
     subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", str(so), *sources, "-lm"])
     lib = oracle.configure(ctypes.CDLL(str(so)))
     saved = oracle._lib
@@ -149,4 +185,10 @@ def test_tree_pins_catch_mutation(tmp_path, mid, old, new):
 @pytest.mark.parametrize("mid,old,new", ACCEPT_MUTATIONS, ids=[m[0] for m in ACCEPT_MUTATIONS])
 def test_accept_pins_catch_mutation(tmp_path, mid, old, new):
     failed = _run_mutation(tmp_path, SRC_ACCEPT, mid, old, new, ACCEPT_PINS)
+    assert failed, f"no pin caught mutation {mid}"
+
+
+@pytest.mark.parametrize("mid,old,new", NEIGHBOUR_MUTATIONS, ids=[m[0] for m in NEIGHBOUR_MUTATIONS])
+def test_neighbour_pins_catch_mutation(tmp_path, mid, old, new):
+    failed = _run_mutation(tmp_path, SRC_NEIGHBOUR, mid, old, new, NEIGHBOUR_PINS)
     assert failed, f"no pin caught mutation {mid}"

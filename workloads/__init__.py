@@ -291,3 +291,32 @@ def sample_rows(w: Workload, n: int, seed: int = 7) -> np.ndarray:
         local = rng.choice(w.Q * w.H, size=k, replace=False)
         rows.append(b * w.Q * w.H + np.sort(local))
     return np.concatenate(rows).astype(np.int64)
+
+
+# --------------------------------------------------------------------------- around the attention
+# Rotary base of the synthetic model (a configuration value, as in Kimi K2-style configs).
+ROPE_THETA = 50000.0
+
+
+@dataclass
+class NeighbourInputs:
+    """Synthetic tensors of the steps around the verify attention for B trees of Q nodes."""
+    q: np.ndarray        # float32 [B][Q][H][d_nope + 64]: query projection (nope part, then rope part)
+    w_kc: np.ndarray     # float32 [H][d_nope][512]: absorb weights (nope -> latent)
+    w_vc: np.ndarray     # float32 [H][d_v][512]: value weights (latent -> value)
+    latent: np.ndarray   # float32 [B][Q][512]: the nodes' new latent cache rows
+    k_pe: np.ndarray     # float32 [B][Q][64]: the nodes' new rope keys, not yet rotated
+    theta: float
+
+
+def neighbour_inputs(seed: int, B: int, Q: int, H: int, d_nope: int = 128, d_v: int = 128,
+                     theta: float = ROPE_THETA) -> NeighbourInputs:
+    """Seeded draws, in this order: q ~ N(0,1), w_kc ~ N(0, 1/d_nope), w_vc ~ N(0, 1/512),
+    latent ~ N(0,1), k_pe ~ N(0,1).  The weight spreads keep q_abs and v near unit scale."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Q, H, d_nope + D_ROPE), dtype=np.float32)
+    w_kc = rng.standard_normal((H, d_nope, D_LATENT), dtype=np.float32) * np.float32(1.0 / math.sqrt(d_nope))
+    w_vc = rng.standard_normal((H, d_v, D_LATENT), dtype=np.float32) * np.float32(1.0 / math.sqrt(D_LATENT))
+    latent = rng.standard_normal((B, Q, D_LATENT), dtype=np.float32)
+    k_pe = rng.standard_normal((B, Q, D_ROPE), dtype=np.float32)
+    return NeighbourInputs(q=q, w_kc=w_kc, w_vc=w_vc, latent=latent, k_pe=k_pe, theta=float(theta))
