@@ -325,6 +325,76 @@ ddtv_status ddtv_tree_accept(const float *logits, int32_t V, const int32_t *pare
                              ddtv_dtype kv_dtype, int32_t *pred, int32_t *path,
                              int32_t *out_tokens, int32_t *accept_len, hipStream_t stream);
 
+/*
+ * The steps around the attention (query preparation before it, the value
+ * projection after it, the tree's new cache rows before both).
+ *   Pages: "The Query-Split Kernel: A Pivotal Edit in Building a Native DDTree
+ *   Inference Engine", sections "The Reasoning Chain" and "Input Knowledge" (the
+ *   query projection of each token and head is a nope part followed by a rope
+ *   part; the rope part gets NeoX rotary embedding with float64 angles; the nope
+ *   part is absorbed into latent space through w_kc; the new key-value latents
+ *   and rope keys are written to the cache); "The Verify-Attn Kernel ...",
+ *   section "Design Decisions and Trade-Offs" (the attention returns the latent;
+ *   a separate per-head GEMM with w_vc follows).
+ *
+ * Rotary embedding (NeoX, rotate-half form): pair i of a 64-wide vector x is
+ * (x[i], x[i + 32]), i < 32; at position p it turns by a = p * theta^(-2i/64)
+ * radians:  y[i] = x[i] cos a - x[i+32] sin a,  y[i+32] = x[i+32] cos a + x[i] sin a.
+ * Frequencies, angles, sine, cosine and the rotation run in float64; results are
+ * rounded once.  rope_theta: the rotary base (finite, > 0).
+ *
+ * Positions: node i of batch row b sits at position prefix[b] + depth(i) (root
+ * depth 0), the position its token takes once its path is appended to the
+ * prefix.  `positions` (DEVICE int32 [B][Q], or NULL) overrides this; when NULL
+ * the depth is read from the ancestor-or-self masks of `vis` (depth + 1 bits).
+ */
+
+/*
+ * Query preparation for the verify attention, in one launch: split, rotate, absorb.
+ *   q       DEVICE float [B][Q][H][d_nope + 64]: the query projection of every
+ *           tree node and head, nope part first (16-byte aligned)
+ *   d_nope  width of the nope part: a multiple of 32 in 32..512
+ *   vis     HOST struct from ddtv_build_visibility (B, Q and, when positions is
+ *           NULL, the masks and row table; complete on `stream` when this runs)
+ *   w_kc    DEVICE float [H][d_nope][512]: per-head absorb weights
+ *   q_abs   DEVICE float [B][Q][H][512] out: q_abs[.., c] = sum_k nope[k] w_kc[h][k][c]
+ *   q_rope  DEVICE float [B][Q][H][64] out: the rope part, rotated
+ * The outputs are exactly the q_abs / q_rope operands of ddtv_verify_attn.
+ * Errors: DDTV_EINVAL (null or misaligned pointers, H outside 1..1024, bad theta,
+ * bad vis), DDTV_EUNSUPPORTED (d_nope, more than 2^30 nodes), DDTV_EDEVICE.
+ */
+ddtv_status ddtv_prepare_query(const float *q, int32_t d_nope, int32_t H, const ddtv_vis *vis,
+                               const int32_t *positions, double rope_theta, const float *w_kc,
+                               float *q_abs, float *q_rope, hipStream_t stream);
+
+/*
+ * Per-head value projection of the attention output (the separate GEMM after it).
+ *   latent  DEVICE float [M][H][512]: ddtv_verify_attn's `out` (M = B * Q), 16-byte aligned
+ *   w_vc    DEVICE float [H][d_v][512]: per-head value weights (16-byte aligned)
+ *   v       DEVICE float [M][H][d_v] out: v[m][h][n] = sum_c latent[m][h][c] w_vc[h][n][c]
+ *   d_v     1..512
+ * M = 0 is a no-op.  Errors: DDTV_EINVAL (null or misaligned pointers, M < 0,
+ * H outside 1..1024), DDTV_EUNSUPPORTED (d_v, M above 2^30), DDTV_EDEVICE.
+ */
+ddtv_status ddtv_value_proj(const float *latent, int64_t M, int32_t H, int32_t d_v, const float *w_vc,
+                            float *v, hipStream_t stream);
+
+/*
+ * The tree nodes' new cache rows: node i of batch row b writes latent[b][i] and
+ * its rope key rotated at its position to cache row kv_off(b) + prefix[b] + i
+ * (the rows ddtv_verify_attn reads for the tree).  Other rows are untouched.
+ *   latent  DEVICE float [B][Q][512] (16-byte aligned); k_pe DEVICE float [B][Q][64]
+ *   vis, positions, rope_theta  as above
+ *   ckv, k_rope  DEVICE caches ([total_kv][512], [total_kv][64]) of kv_dtype; bf16
+ *           caches receive round-to-nearest-even values (finite inputs); ckv
+ *           16-byte aligned
+ * Errors: DDTV_EINVAL (null or misaligned pointers, bad theta, bad vis),
+ * DDTV_EUNSUPPORTED (dtype), DDTV_EDEVICE.
+ */
+ddtv_status ddtv_append_kv(const float *latent, const float *k_pe, const ddtv_vis *vis,
+                           const int32_t *positions, double rope_theta, void *ckv, void *k_rope,
+                           ddtv_dtype kv_dtype, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *ddtv_status_string(ddtv_status s);
 

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert dd.ddtv_version() == 600
+    assert dd.ddtv_version() == 700
     for code in range(6):
         assert dd.ddtv_status_string(code)
     assert dd.ddtv_status_string(2).startswith("malformed tree")
@@ -193,6 +193,52 @@ def test_tail_mode_argument_checks(lib):
     assert call(ws=None) == dd.DDTV_EWORKSPACE
     assert call(ws_bytes=need - 1) == dd.DDTV_EWORKSPACE
     assert call(ws=FAKE + 16) == dd.DDTV_EINVAL           # workspace must be 256-byte aligned
+
+
+def test_neighbour_argument_checks(lib):
+    """Host checks of query preparation, value projection and cache append come before any HIP call."""
+    E, U = dd.DDTV_EINVAL, dd.DDTV_EUNSUPPORTED
+    vis = fake_vis(B=2, Q=9)
+
+    def prep(q=FAKE, d_nope=128, H=8, v=vis, pos=None, theta=50000.0, w=FAKE, qa=FAKE, qr=FAKE):
+        return lib.ddtv_prepare_query(q, d_nope, H, ctypes.byref(v.vis) if v is not None else None, pos, theta,
+                                      w, qa, qr, None)
+
+    assert prep(q=None) == E
+    assert prep(w=None) == E
+    assert prep(qa=FAKE + 8) == E                  # 16-byte alignment
+    assert prep(pos=FAKE + 2) == E
+    assert prep(v=None) == E
+    assert prep(H=0) == E
+    assert prep(H=1025) == E
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert prep(theta=bad) == E
+    for d in (0, 16, 48, 544):
+        assert prep(d_nope=d) == U
+
+    def vproj(lat=FAKE, M=18, H=8, d_v=128, w=FAKE, v=FAKE):
+        return lib.ddtv_value_proj(lat, M, H, d_v, w, v, None)
+
+    assert vproj(lat=None) == E
+    assert vproj(v=None) == E
+    assert vproj(lat=FAKE + 4) == E
+    assert vproj(M=-1) == E
+    assert vproj(H=0) == E
+    assert vproj(d_v=0) == U
+    assert vproj(d_v=513) == U
+    assert vproj(M=(1 << 30) + 1) == U
+    assert vproj(M=0) == dd.DDTV_OK                 # nothing to do, nothing launched
+
+    def app(lat=FAKE, kpe=FAKE, v=vis, pos=None, theta=50000.0, ckv=FAKE, kr=FAKE, dtype=0):
+        return lib.ddtv_append_kv(lat, kpe, ctypes.byref(v.vis) if v is not None else None, pos, theta, ckv, kr,
+                                  dtype, None)
+
+    assert app(lat=None) == E
+    assert app(kr=None) == E
+    assert app(ckv=FAKE + 8) == E
+    assert app(v=None) == E
+    assert app(theta=0.0) == E
+    assert app(dtype=7) == U
 
 
 def test_plan_rules(lib):

@@ -28,7 +28,8 @@ EXPORTED = (
     "ddtv_vis_bytes", "ddtv_build_visibility", "ddtv_read_status", "ddtv_workspace_bytes",
     "ddtv_workspace_bytes_ex", "ddtv_verify_attn", "ddtv_verify_attn_ex", "ddtv_plan_info",
     "ddtv_status_string", "ddtv_version", "ddtv_build_tree", "ddtv_tree_accept",
-    "ddtv_tail_workspace_bytes", "ddtv_verify_attn_tail",
+    "ddtv_tail_workspace_bytes", "ddtv_verify_attn_tail", "ddtv_prepare_query", "ddtv_value_proj",
+    "ddtv_append_kv",
 )
 
 
@@ -92,6 +93,13 @@ def load(path: str = LIB_PATH):
     lib.ddtv_tail_workspace_bytes.restype = sz
     lib.ddtv_verify_attn_tail.argtypes = [P, P, P, P, ctypes.c_int, i32, VP, ctypes.c_float, P, P, P, P, P, sz, P, OP]
     lib.ddtv_verify_attn_tail.restype = ctypes.c_int
+    f64 = ctypes.c_double
+    lib.ddtv_prepare_query.argtypes = [P, i32, i32, VP, P, f64, P, P, P, P]
+    lib.ddtv_prepare_query.restype = ctypes.c_int
+    lib.ddtv_value_proj.argtypes = [P, ctypes.c_int64, i32, i32, P, P, P]
+    lib.ddtv_value_proj.restype = ctypes.c_int
+    lib.ddtv_append_kv.argtypes = [P, P, VP, P, f64, P, P, ctypes.c_int, P]
+    lib.ddtv_append_kv.restype = ctypes.c_int
     lib.ddtv_status_string.argtypes = [ctypes.c_int]
     lib.ddtv_status_string.restype = ctypes.c_char_p
     lib.ddtv_version.argtypes = []
@@ -240,6 +248,28 @@ def ddtv_verify_attn(q_abs, q_rope, ckv, k_rope, kv_dtype: int, H: int, vis: Vis
     if opts is None:
         return lib.ddtv_verify_attn(*args)
     return lib.ddtv_verify_attn_ex(*args, ctypes.byref(opts))
+
+
+def ddtv_prepare_query(q, w_kc, vis: Visibility, q_abs, q_rope, rope_theta: float, positions=None,
+                       stream=None) -> int:
+    """q: device float32 [B][Q][H][d_nope + 64]; w_kc: [H][d_nope][512]; outputs [B][Q][H][512], [B][Q][H][64]."""
+    H, row = int(q.shape[-2]), int(q.shape[-1])
+    return load().ddtv_prepare_query(_ptr(q), row - 64, H, ctypes.byref(vis.vis), _ptr(positions),
+                                     float(rope_theta), _ptr(w_kc), _ptr(q_abs), _ptr(q_rope), _stream(stream))
+
+
+def ddtv_value_proj(latent, w_vc, v, stream=None) -> int:
+    """latent: device float32 [..., H, 512]; w_vc: [H][d_v][512]; v: [..., H, d_v]."""
+    H, d_v = int(w_vc.shape[0]), int(w_vc.shape[1])
+    M = latent.numel() // (H * 512)
+    return load().ddtv_value_proj(_ptr(latent), M, H, d_v, _ptr(w_vc), _ptr(v), _stream(stream))
+
+
+def ddtv_append_kv(latent, k_pe, vis: Visibility, ckv, k_rope, kv_dtype: int, rope_theta: float, positions=None,
+                   stream=None) -> int:
+    """latent: device float32 [B][Q][512]; k_pe: [B][Q][64]; caches [total_kv][512], [total_kv][64]."""
+    return load().ddtv_append_kv(_ptr(latent), _ptr(k_pe), ctypes.byref(vis.vis), _ptr(positions),
+                                 float(rope_theta), _ptr(ckv), _ptr(k_rope), kv_dtype, _stream(stream))
 
 
 ddtv_verify_attn_ex = ddtv_verify_attn

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <functional>
 #include <mutex>
 #include <queue>
@@ -18,7 +19,7 @@ using namespace ddtv;
 
 namespace {
 
-constexpr int32_t kVersion = 600;   // 0.6.0: external-prefix (tree-tail) mode
+constexpr int32_t kVersion = 700;   // 0.7.0: query preparation, value projection, appended cache rows
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -60,6 +61,16 @@ int cu_count() {
         cached[dev] = n;
     }
     return cached[dev];
+}
+
+constexpr int32_t kMaxProjHeads = 1024;          // heads per projection call (grid z)
+constexpr int64_t kMaxProjRows = (int64_t)1 << 30; // tokens per projection call (grid x * 256 threads < 2^32)
+
+bool rope_ok(double theta) { return std::isfinite(theta) && theta > 0.0; }
+
+// Rotary frequency of pair i (of 32): theta^(-2i/64), in float64.
+void rope_frequencies(double theta, double* f) {
+    for (int i = 0; i < kDRope / 2; ++i) f[i] = pow(theta, -(double)(2 * i) / (double)kDRope);
 }
 
 ddtv_status check_vis(const ddtv_vis* vis) {
@@ -592,6 +603,92 @@ ddtv_status ddtv_verify_attn_ex(const float* q_abs, const float* q_rope, const v
     if (opts && opts->attn_end && hipEventRecord(opts->attn_end, stream) != hipSuccess) return DDTV_EDEVICE;
     if (p.n_split > 1 && launch_merge(a, stream) != hipSuccess) return DDTV_EDEVICE;
     return DDTV_OK;
+}
+
+ddtv_status ddtv_prepare_query(const float* q, int32_t d_nope, int32_t H, const ddtv_vis* vis,
+                               const int32_t* positions, double rope_theta, const float* w_kc, float* q_abs,
+                               float* q_rope, hipStream_t stream) {
+    if (!q || !w_kc || !q_abs || !q_rope) return DDTV_EINVAL;
+    if (!aligned(q, 16) || !aligned(w_kc, 16) || !aligned(q_abs, 16) || !aligned(q_rope, 16) ||
+        !aligned(positions, 4))
+        return DDTV_EINVAL;
+    ddtv_status st = check_vis(vis);
+    if (st) return st;
+    if (H < 1 || H > kMaxProjHeads || !rope_ok(rope_theta)) return DDTV_EINVAL;
+    if (d_nope < 32 || d_nope > 512 || d_nope % 32 != 0) return DDTV_EUNSUPPORTED;
+    if ((int64_t)vis->B * vis->Q > kMaxProjRows) return DDTV_EUNSUPPORTED;
+    ProjArgs p{};
+    p.M = (int64_t)vis->B * vis->Q;
+    p.K = d_nope;
+    p.N = kDLat;
+    p.H = H;
+    p.A = q;
+    p.a_head = d_nope + kDRope;
+    p.lda = (int64_t)H * p.a_head;
+    p.B = w_kc;
+    p.b_head = (int64_t)d_nope * kDLat;
+    p.C = q_abs;
+    p.c_head = kDLat;
+    p.ldc = (int64_t)H * kDLat;
+    p.rope_out = q_rope;
+    p.positions = positions;
+    p.bits = vis->bits;
+    p.rows = vis->rows;
+    p.Q = vis->Q;
+    p.W = vis->W;
+    rope_frequencies(rope_theta, p.inv_freq);
+    return launch_proj(p, false, stream) == hipSuccess ? DDTV_OK : DDTV_EDEVICE;
+}
+
+ddtv_status ddtv_value_proj(const float* latent, int64_t M, int32_t H, int32_t d_v, const float* w_vc, float* v,
+                            hipStream_t stream) {
+    if (!latent || !w_vc || !v) return DDTV_EINVAL;
+    if (!aligned(latent, 16) || !aligned(w_vc, 16) || !aligned(v, 4)) return DDTV_EINVAL;
+    if (M < 0 || H < 1 || H > kMaxProjHeads) return DDTV_EINVAL;
+    if (M > kMaxProjRows) return DDTV_EUNSUPPORTED;
+    if (d_v < 1 || d_v > kDLat) return DDTV_EUNSUPPORTED;
+    if (M == 0) return DDTV_OK;
+    ProjArgs p{};
+    p.M = M;
+    p.K = kDLat;
+    p.N = d_v;
+    p.H = H;
+    p.A = latent;
+    p.a_head = kDLat;
+    p.lda = (int64_t)H * kDLat;
+    p.B = w_vc;
+    p.b_head = (int64_t)d_v * kDLat;
+    p.C = v;
+    p.c_head = d_v;
+    p.ldc = (int64_t)H * d_v;
+    return launch_proj(p, true, stream) == hipSuccess ? DDTV_OK : DDTV_EDEVICE;
+}
+
+ddtv_status ddtv_append_kv(const float* latent, const float* k_pe, const ddtv_vis* vis, const int32_t* positions,
+                           double rope_theta, void* ckv, void* k_rope, ddtv_dtype kv_dtype, hipStream_t stream) {
+    if (!latent || !k_pe || !ckv || !k_rope) return DDTV_EINVAL;
+    if (!aligned(latent, 16) || !aligned(k_pe, 4) || !aligned(ckv, 16) || !aligned(k_rope, 4) ||
+        !aligned(positions, 4))
+        return DDTV_EINVAL;
+    ddtv_status st = check_vis(vis);
+    if (st) return st;
+    if (!rope_ok(rope_theta)) return DDTV_EINVAL;
+    if (kv_dtype != DDTV_F32 && kv_dtype != DDTV_BF16) return DDTV_EUNSUPPORTED;
+    if ((int64_t)vis->B * vis->Q > (int64_t)INT32_MAX) return DDTV_EUNSUPPORTED;
+    AppendArgs p{};
+    p.latent = latent;
+    p.k_pe = k_pe;
+    p.positions = positions;
+    p.bits = vis->bits;
+    p.rows = vis->rows;
+    p.ckv = ckv;
+    p.k_rope = k_rope;
+    p.B = vis->B;
+    p.Q = vis->Q;
+    p.W = vis->W;
+    p.bf16 = kv_dtype == DDTV_BF16;
+    rope_frequencies(rope_theta, p.inv_freq);
+    return launch_append_kv(p, stream) == hipSuccess ? DDTV_OK : DDTV_EDEVICE;
 }
 
 ddtv_status ddtv_verify_attn(const float* q_abs, const float* q_rope, const void* ckv, const void* k_rope,

@@ -1,0 +1,274 @@
+// The steps around the verify attention: the query split with NeoX rotary
+// embedding and the w_kc absorb before it, the w_vc value projection after it,
+// and the tree nodes' new cache rows (latent plus rotated rope key).
+//   Pages: "The Query-Split Kernel: A Pivotal Edit in Building a Native DDTree
+//   Inference Engine", sections "The Reasoning Chain" and "Input Knowledge"
+//   (the query projection of each token and head holds a nope part and a rope
+//   part; the rope part is rotated NeoX style with float64 angles; the nope part
+//   meets the latent through the absorbed w_kc); "The Verify-Attn Kernel ...",
+//   section "Design Decisions and Trade-Offs" (the attention emits the latent, a
+//   separate per-head GEMM with w_vc follows).  The pages split the query into
+//   contiguous nope/rope buffers with one kernel, rotate with another and absorb
+//   with a GEMM; here one launch reads the projection once and writes both
+//   attention operands.
+//
+// Both projections are per-head fp32 GEMMs on the matrix cores
+// (v_mfma_f32_16x16x4_f32), C[m][n] = sum_k A[m][k] B[k][n] for every head:
+//   absorb:  A = q[m][h][0..d_nope), B = w_kc[h] ([d_nope][512]), C = q_abs[m][h]
+//   value:   A = latent[m][h][0..512), B = w_vc[h]^T (w_vc[h] is [d_v][512]),
+//            C = v[m][h]
+// A workgroup (4 waves) owns a 64 x 128 output tile of one head and walks K in
+// stages of 32, double-buffered through LDS: 16-byte global loads, the next
+// stage loaded into registers while the current one feeds the MFMAs.  Each wave
+// owns 32 x 64 of the tile (2 x 4 blocks of 16 x 16).
+// LDS layouts (4-byte words; 64 banks on gfx950):
+//   A stage   [64 m][36]   : lane (i, kk) of an A operand reads m = i, k = kk;
+//                            row stride 36 words puts the 16 x 4 lanes on 64
+//                            distinct banks;
+//   B stage   absorb: [32 k][144] (n contiguous; stride 144 = 16 mod 64 puts the
+//                            four k rows of an operand on disjoint bank groups)
+//             value:  [128 n][36] (k contiguous, as A).
+#include <math.h>
+
+#include "ddtv_internal.hpp"
+
+namespace ddtv {
+namespace {
+
+constexpr int kBM = 64, kBN = 128, kBK = 32;
+constexpr int kThreadsProj = 256;
+constexpr int kAStride = 36;             // words per m row of an A stage
+constexpr int kBStrideKN = 144;          // words per k row of a [k][n] B stage
+constexpr int kBStrideNK = 36;           // words per n row of an [n][k] B stage
+constexpr int kAStage = kBM * kAStride;                  // 2304 words
+constexpr int kBStage = kBK * kBStrideKN;                // 4608 words (= kBN * kBStrideNK)
+static_assert(kBK * kBStrideKN == kBN * kBStrideNK, "both B layouts fill the same stage");
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+// Global -> registers for one K stage.  A: 64 rows x 32 k = 512 float4, two per
+// thread (8 threads per row, 128 contiguous bytes).  B: 1024 float4, four per
+// thread: [k][n] rows of 512 bytes, or [n][k] rows of 128 bytes.
+template <bool kBTrans>
+struct Stage {
+    float4 a[2];
+    float4 b[4];
+};
+
+template <bool kBTrans>
+__device__ __forceinline__ void load_stage(const ProjArgs& p, int h, int m0, int n0, int k0, Stage<kBTrans>& s) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int idx = t + r * kThreadsProj;
+        const int row = idx >> 3, kq = (idx & 7) * 4;
+        const int64_t m = (int64_t)m0 + row;
+        s.a[r] = m < p.M ? ld4(p.A + m * p.lda + (int64_t)h * p.a_head + k0 + kq) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int idx = t + r * kThreadsProj;
+        if (!kBTrans) {
+            const int k = idx >> 5, nq = (idx & 31) * 4;       // 32 float4 per k row
+            const int n = n0 + nq;
+            s.b[r] = n < p.N ? ld4(p.B + (int64_t)h * p.b_head + (int64_t)(k0 + k) * p.N + n)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+        } else {
+            const int nl = idx >> 3, kq = (idx & 7) * 4;       // 8 float4 per n row
+            const int n = n0 + nl;
+            s.b[r] = n < p.N ? ld4(p.B + (int64_t)h * p.b_head + (int64_t)n * p.K + k0 + kq)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+}
+
+template <bool kBTrans>
+__device__ __forceinline__ void store_stage(float* As, float* Bs, const Stage<kBTrans>& s) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int idx = t + r * kThreadsProj;
+        const int row = idx >> 3, kq = (idx & 7) * 4;
+        *reinterpret_cast<float4*>(As + row * kAStride + kq) = s.a[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int idx = t + r * kThreadsProj;
+        if (!kBTrans) {
+            const int k = idx >> 5, nq = (idx & 31) * 4;
+            *reinterpret_cast<float4*>(Bs + k * kBStrideKN + nq) = s.b[r];
+        } else {
+            const int nl = idx >> 3, kq = (idx & 7) * 4;
+            *reinterpret_cast<float4*>(Bs + nl * kBStrideNK + kq) = s.b[r];
+        }
+    }
+}
+
+// NeoX rotation of the rope part of 64 query rows (m0 .. m0+63) of head h.
+// Angles, their sine and cosine, and the rotation run in float64; the result is
+// rounded once to float32.
+__device__ void rope_rows(const ProjArgs& p, int h, int m0) {
+    for (int idx = threadIdx.x; idx < kBM * 32; idx += kThreadsProj) {
+        const int64_t m = (int64_t)m0 + (idx >> 5);
+        const int i = idx & 31;
+        if (m >= p.M) break;
+        int32_t pos;
+        if (p.positions) {
+            pos = p.positions[m];
+        } else {   // prefix length plus depth: the ancestor-or-self mask holds depth + 1 bits
+            const int b = (int)(m / p.Q), q = (int)(m % p.Q);
+            const uint32_t* w = p.bits + ((int64_t)b * p.Q + q) * p.W;
+            int pc = 0;
+            for (int k = 0; k < p.W; ++k) pc += __popc(w[k]);
+            pos = p.rows[b].prefix + pc - 1;
+        }
+        const float* x = p.A + m * p.lda + (int64_t)h * p.a_head + p.K;
+        const double x0 = (double)x[i], x1 = (double)x[i + 32];
+        double sn, cs;
+        sincos((double)pos * p.inv_freq[i], &sn, &cs);
+        float* y = p.rope_out + (m * p.H + h) * kDRope;
+        y[i] = (float)(x0 * cs - x1 * sn);
+        y[i + 32] = (float)(x1 * cs + x0 * sn);
+    }
+}
+
+template <bool kBTrans>
+__global__ __launch_bounds__(kThreadsProj) void proj_gemm_kernel(ProjArgs p) {
+    __shared__ float As[2][kAStage];
+    __shared__ float Bs[2][kBStage];
+    const int h = blockIdx.z;
+    const int m0 = blockIdx.x * kBM, n0 = blockIdx.y * kBN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 64;
+    const int li = lane & 15, lk = lane >> 4;
+
+    if (!kBTrans && p.rope_out && blockIdx.y == 0) rope_rows(p, h, m0);
+
+    floatx4 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    Stage<kBTrans> st;
+    load_stage<kBTrans>(p, h, m0, n0, 0, st);
+    store_stage<kBTrans>(As[0], Bs[0], st);
+    __syncthreads();
+    const int n_stage = p.K / kBK;
+    for (int s = 0; s < n_stage; ++s) {
+        const int cur = s & 1;
+        if (s + 1 < n_stage) load_stage<kBTrans>(p, h, m0, n0, (s + 1) * kBK, st);
+        const float* A = As[cur];
+        const float* Bm = Bs[cur];
+#pragma unroll
+        for (int kk = 0; kk < kBK; kk += 4) {
+            float a[2], b[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) a[i] = A[(wm + i * 16 + li) * kAStride + kk + lk];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                b[j] = kBTrans ? Bm[(wn + j * 16 + li) * kBStrideNK + kk + lk]
+                               : Bm[(kk + lk) * kBStrideKN + wn + j * 16 + li];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        if (s + 1 < n_stage) {
+            store_stage<kBTrans>(As[cur ^ 1], Bs[cur ^ 1], st);
+            __syncthreads();
+        }
+    }
+    // D block (i, j): lane holds rows 4*lk + r, column li.
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t m = (int64_t)m0 + wm + i * 16 + 4 * lk + r;
+            if (m >= p.M) continue;
+            float* c = p.C + m * p.ldc + (int64_t)h * p.c_head;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = n0 + wn + j * 16 + li;
+                if (n < p.N) c[n] = acc[i][j][r];
+            }
+        }
+    }
+}
+
+// Float32 -> bf16 bits, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// One wave per tree node: its latent row and its rotated rope key go to cache
+// row kv_off + prefix + node.
+__global__ __launch_bounds__(64) void append_kv_kernel(AppendArgs p) {
+    const int64_t node = blockIdx.x;
+    const int b = (int)(node / p.Q), q = (int)(node % p.Q);
+    const int lane = threadIdx.x;
+    const ddtv_row row = p.rows[b];
+    const int64_t r = row.kv_off + row.prefix + q;
+    int32_t pos;
+    if (p.positions) {
+        pos = p.positions[node];
+    } else {
+        const uint32_t* w = p.bits + node * p.W;
+        int pc = 0;
+        for (int k = 0; k < p.W; ++k) pc += __popc(w[k]);
+        pos = row.prefix + pc - 1;
+    }
+    const float* lat = p.latent + node * kDLat;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int c = (lane + u * 64) * 4;
+        const float4 v = ld4(lat + c);
+        if (p.bf16) {
+            uint16_t* d = reinterpret_cast<uint16_t*>(p.ckv) + r * kDLat + c;
+            ushort4 o;
+            o.x = to_bf16(v.x); o.y = to_bf16(v.y); o.z = to_bf16(v.z); o.w = to_bf16(v.w);
+            *reinterpret_cast<ushort4*>(d) = o;
+        } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.ckv) + r * kDLat + c) = v;
+        }
+    }
+    if (lane < 32) {
+        const float* x = p.k_pe + node * kDRope;
+        const double x0 = (double)x[lane], x1 = (double)x[lane + 32];
+        double sn, cs;
+        sincos((double)pos * p.inv_freq[lane], &sn, &cs);
+        const float y0 = (float)(x0 * cs - x1 * sn), y1 = (float)(x1 * cs + x0 * sn);
+        if (p.bf16) {
+            uint16_t* d = reinterpret_cast<uint16_t*>(p.k_rope) + r * kDRope;
+            d[lane] = to_bf16(y0);
+            d[lane + 32] = to_bf16(y1);
+        } else {
+            float* d = reinterpret_cast<float*>(p.k_rope) + r * kDRope;
+            d[lane] = y0;
+            d[lane + 32] = y1;
+        }
+    }
+}
+
+}  // namespace
+
+
+hipError_t launch_proj(const ProjArgs& p, bool b_trans, hipStream_t stream) {
+    const dim3 grid((unsigned)((p.M + kBM - 1) / kBM), (unsigned)((p.N + kBN - 1) / kBN), (unsigned)p.H);
+    if (b_trans)
+        hipLaunchKernelGGL(proj_gemm_kernel<true>, grid, dim3(kThreadsProj), 0, stream, p);
+    else
+        hipLaunchKernelGGL(proj_gemm_kernel<false>, grid, dim3(kThreadsProj), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_kv(const AppendArgs& p, hipStream_t stream) {
+    hipLaunchKernelGGL(append_kv_kernel, dim3((unsigned)((int64_t)p.B * p.Q)), dim3(64), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace ddtv
