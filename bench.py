@@ -206,6 +206,66 @@ def time_tail_mode(dd, hip, stream, r, steps=20, warmup=3):
             "us_per_call": round(us, 2), "calls": steps}
 
 
+def time_neighbour(dd, hip, stream, r, d_nope=128, d_v=128, steps=20, warmup=3):
+    """The steps around the attention at the benchmarked tree and head counts:
+    query preparation (split, rotation, w_kc absorb), the w_vc value projection of
+    the attention output, and the tree's appended cache rows; synthetic weights
+    and projections; average launch times from HIP events."""
+    import torch
+    import workloads as wl
+    w = r.w
+    B, Q, H = w.B, w.Q, w.H
+    M = B * Q
+    dev = r.device
+    nb = wl.neighbour_inputs(7300 + B + Q, B, Q, H, d_nope=d_nope, d_v=d_v)
+    q = torch.from_numpy(nb.q).to(dev)
+    w_kc = torch.from_numpy(nb.w_kc).to(dev)
+    w_vc = torch.from_numpy(nb.w_vc).to(dev)
+    lat = torch.from_numpy(nb.latent).to(dev)
+    k_pe = torch.from_numpy(nb.k_pe).to(dev)
+    q_abs = torch.empty((B, Q, H, 512), dtype=torch.float32, device=dev)
+    q_rope = torch.empty((B, Q, H, 64), dtype=torch.float32, device=dev)
+    v = torch.empty((B, Q, H, d_v), dtype=torch.float32, device=dev)
+
+    def timed(launch):
+        for _ in range(warmup):
+            launch()
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, stream)
+        for _ in range(steps):
+            launch()
+        hip.record(e1, stream)
+        return hip.elapsed_ms(e0, e1) * 1e3 / steps
+
+    def prep():
+        assert dd.ddtv_prepare_query(q, w_kc, r.vis, q_abs, q_rope, nb.theta, stream=stream) == dd.DDTV_OK
+
+    def vproj():
+        assert dd.ddtv_value_proj(r.out, w_vc, v, stream=stream) == dd.DDTV_OK
+
+    def append():
+        assert dd.ddtv_append_kv(lat, k_pe, r.vis, r.ckv, r.k_rope, w.kv_dtype, nb.theta, stream=stream) == dd.DDTV_OK
+
+    elem = 2 if w.kv_dtype == 1 else 4
+    res = {"workload": f"B*Q={M} tree nodes x H={H} heads, d_nope={d_nope}, d_v={d_v}, rope theta {nb.theta:g} "
+                       "(synthetic weights and projections)"}
+    for name, fn, flops, nbytes in (
+            ("prepare_query", prep, 2 * M * H * d_nope * 512, 4 * (M * H * (d_nope + 64) + H * d_nope * 512
+                                                                   + M * H * (512 + 64))),
+            ("value_proj", vproj, 2 * M * H * 512 * d_v, 4 * (M * H * 512 + H * d_v * 512 + M * H * d_v)),
+            ("append_kv", append, 0, 4 * M * (512 + 64) + elem * M * (512 + 64))):
+        us = timed(fn)
+        item = {"us_per_launch": round(us, 2), "algorithmic_bytes": nbytes,
+                "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        if flops:
+            item["flops"] = flops
+            item["tflops"] = round(flops / (us * 1e-6) / 1e12, 2)
+            item["frac_of_fp32_mfma_peak"] = round(flops / (us * 1e-6) / 1e12 / PEAK_TFLOPS["f32-mfma"], 4)
+        res[name] = item
+    res["launches"] = steps
+    return res
+
+
 def cpu_baseline(w, budget_s=15.0, max_rows=4096):
     """The oracle (single-threaded fp64 C) on a seeded sample of query rows of the
     same workload, for about budget_s seconds.  Reported as tree-query tokens/s
@@ -358,6 +418,7 @@ def main():
     out["tree_build"] = time_tree_builder(dd, hip, stream, dev, w.B, w.Q)
     out["tail_mode"] = time_tail_mode(dd, hip, stream, r)
     out["tree_accept"] = time_tree_accept(dd, hip, stream, r)
+    out["neighbour"] = time_neighbour(dd, hip, stream, r)
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(w, budget_s=args.cpu_budget)

@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "ddtv_internal.hpp"
+#include "neighbour.hpp"
 #include "tail.hpp"
 
 using namespace ddtv;

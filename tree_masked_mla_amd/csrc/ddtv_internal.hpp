@@ -69,40 +69,6 @@ struct AcceptArgs {
     int B, Q, V;
 };
 
-// A per-head projection GEMM (absorb or value), optionally with the query's
-// rotary step (passed by value).  A[m][h][k] = A[m * lda + h * a_head + k];
-// the head-h block of B is [K][N] (absorb) or [N][K] (value);
-// C[m][h][n] = C[m * ldc + h * c_head + n].
-struct ProjArgs {
-    const float* A;
-    int64_t lda, a_head;
-    const float* B;
-    int64_t b_head;
-    float* C;
-    int64_t ldc, c_head;
-    int64_t M;
-    int K, N, H;
-    float* rope_out;            // [M][H][64], or null: no rotary step
-    const int32_t* positions;   // [M], or null: prefix + depth from the masks
-    const uint32_t* bits;       // [B][Q][W] ancestor-or-self masks
-    const ddtv_row* rows;       // [B]
-    int Q, W;
-    double inv_freq[32];        // rotary frequency of each pair
-};
-
-// The tree nodes' new cache rows (passed by value).
-struct AppendArgs {
-    const float* latent;        // [B][Q][512]
-    const float* k_pe;          // [B][Q][64], not yet rotated
-    const int32_t* positions;   // [B][Q], or null: prefix + depth from the masks
-    const uint32_t* bits;       // [B][Q][W]
-    const ddtv_row* rows;       // [B]
-    void* ckv;                  // [total_kv][512] f32 or bf16
-    void* k_rope;               // [total_kv][64]
-    int B, Q, W, bf16;
-    double inv_freq[32];
-};
-
 struct VisChunk {
     int64_t kv_off[kVisChunk];
     int32_t prefix[kVisChunk];
@@ -121,8 +87,6 @@ int bf16_rows_per_workgroup();   // query rows per workgroup of the bf16 MFMA ke
 hipError_t launch_merge(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_tree_build(const TreeArgs& a, hipStream_t stream);
 hipError_t launch_tree_accept(const AcceptArgs& a, hipStream_t stream);
-hipError_t launch_proj(const ProjArgs& p, bool b_trans, hipStream_t stream);
-hipError_t launch_append_kv(const AppendArgs& p, hipStream_t stream);
 
 constexpr int kValuRows = 16;   // query rows per VALU workgroup
 

@@ -17,10 +17,11 @@
 //   absorb:  A = q[m][h][0..d_nope), B = w_kc[h] ([d_nope][512]), C = q_abs[m][h]
 //   value:   A = latent[m][h][0..512), B = w_vc[h]^T (w_vc[h] is [d_v][512]),
 //            C = v[m][h]
-// A workgroup (4 waves) owns a 64 x 128 output tile of one head and walks K in
+// A workgroup (8 waves) owns a 64 x 128 output tile of one head and walks K in
 // stages of 32, double-buffered through LDS: 16-byte global loads, the next
 // stage loaded into registers while the current one feeds the MFMAs.  Each wave
-// owns 32 x 64 of the tile (2 x 4 blocks of 16 x 16).
+// owns 32 x 32 of the tile (2 x 2 blocks of 16 x 16); two workgroups fit a CU,
+// so every SIMD holds up to four waves to cover LDS reads and barriers.
 // LDS layouts (4-byte words; 64 banks on gfx950):
 //   A stage   [64 m][36]   : lane (i, kk) of an A operand reads m = i, k = kk;
 //                            row stride 36 words puts the 16 x 4 lanes on 64
@@ -31,12 +32,13 @@
 #include <math.h>
 
 #include "ddtv_internal.hpp"
+#include "neighbour.hpp"
 
 namespace ddtv {
 namespace {
 
 constexpr int kBM = 64, kBN = 128, kBK = 32;
-constexpr int kThreadsProj = 256;
+constexpr int kThreadsProj = 512;
 constexpr int kAStride = 36;             // words per m row of an A stage
 constexpr int kBStrideKN = 144;          // words per k row of a [k][n] B stage
 constexpr int kBStrideNK = 36;           // words per n row of an [n][k] B stage
@@ -48,27 +50,27 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
-// Global -> registers for one K stage.  A: 64 rows x 32 k = 512 float4, two per
-// thread (8 threads per row, 128 contiguous bytes).  B: 1024 float4, four per
+// Global -> registers for one K stage.  A: 64 rows x 32 k = 512 float4, one per
+// thread (8 threads per row, 128 contiguous bytes).  B: 1024 float4, two per
 // thread: [k][n] rows of 512 bytes, or [n][k] rows of 128 bytes.
 template <bool kBTrans>
 struct Stage {
-    float4 a[2];
-    float4 b[4];
+    float4 a[1];
+    float4 b[2];
 };
 
 template <bool kBTrans>
 __device__ __forceinline__ void load_stage(const ProjArgs& p, int h, int m0, int n0, int k0, Stage<kBTrans>& s) {
     const int t = threadIdx.x;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < 1; ++r) {
         const int idx = t + r * kThreadsProj;
         const int row = idx >> 3, kq = (idx & 7) * 4;
         const int64_t m = (int64_t)m0 + row;
         s.a[r] = m < p.M ? ld4(p.A + m * p.lda + (int64_t)h * p.a_head + k0 + kq) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 2; ++r) {
         const int idx = t + r * kThreadsProj;
         if (!kBTrans) {
             const int k = idx >> 5, nq = (idx & 31) * 4;       // 32 float4 per k row
@@ -88,13 +90,13 @@ template <bool kBTrans>
 __device__ __forceinline__ void store_stage(float* As, float* Bs, const Stage<kBTrans>& s) {
     const int t = threadIdx.x;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < 1; ++r) {
         const int idx = t + r * kThreadsProj;
         const int row = idx >> 3, kq = (idx & 7) * 4;
         *reinterpret_cast<float4*>(As + row * kAStride + kq) = s.a[r];
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 2; ++r) {
         const int idx = t + r * kThreadsProj;
         if (!kBTrans) {
             const int k = idx >> 5, nq = (idx & 31) * 4;
@@ -106,31 +108,43 @@ __device__ __forceinline__ void store_stage(float* As, float* Bs, const Stage<kB
     }
 }
 
-// NeoX rotation of the rope part of 64 query rows (m0 .. m0+63) of head h.
-// Angles, their sine and cosine, and the rotation run in float64; the result is
-// rounded once to float32.
-__device__ void rope_rows(const ProjArgs& p, int h, int m0) {
-    for (int idx = threadIdx.x; idx < kBM * 32; idx += kThreadsProj) {
-        const int64_t m = (int64_t)m0 + (idx >> 5);
-        const int i = idx & 31;
-        if (m >= p.M) break;
-        int32_t pos;
-        if (p.positions) {
-            pos = p.positions[m];
-        } else {   // prefix length plus depth: the ancestor-or-self mask holds depth + 1 bits
-            const int b = (int)(m / p.Q), q = (int)(m % p.Q);
-            const uint32_t* w = p.bits + ((int64_t)b * p.Q + q) * p.W;
-            int pc = 0;
-            for (int k = 0; k < p.W; ++k) pc += __popc(w[k]);
-            pos = p.rows[b].prefix + pc - 1;
-        }
-        const float* x = p.A + m * p.lda + (int64_t)h * p.a_head + p.K;
-        const double x0 = (double)x[i], x1 = (double)x[i + 32];
-        double sn, cs;
-        sincos((double)pos * p.inv_freq[i], &sn, &cs);
-        float* y = p.rope_out + (m * p.H + h) * kDRope;
-        y[i] = (float)(x0 * cs - x1 * sn);
-        y[i + 32] = (float)(x1 * cs + x0 * sn);
+// NeoX rotation of the rope part of 32 query rows (m0 .. m0+31), every head.
+// 16 lanes per row, two pairs per lane: each (row, pair) angle is computed once
+// and used for all heads.  Angles, their sine and cosine, and the rotation run
+// in float64; the result is rounded once to float32.
+constexpr int kRopeRows = kThreadsProj / 16;
+static_assert(kDLat / kBN * kRopeRows >= kBM, "the rotary slice covers a row tile with its column-tile workgroups");
+
+__device__ void rope_rows(const ProjArgs& p, int64_t m0) {
+    const int64_t m = m0 + (threadIdx.x >> 4);
+    const int i = (threadIdx.x & 15) * 2;
+    if (m >= p.M) return;
+    int32_t pos;
+    if (p.positions) {
+        pos = p.positions[m];
+    } else {   // prefix length plus depth: the ancestor-or-self mask holds depth + 1 bits
+        const int b = (int)(m / p.Q), q = (int)(m % p.Q);
+        const uint32_t* w = p.bits + ((int64_t)b * p.Q + q) * p.W;
+        int pc = 0;
+        for (int k = 0; k < p.W; ++k) pc += __popc(w[k]);
+        pos = p.rows[b].prefix + pc - 1;
+    }
+    double s0, c0, s1, c1;
+    sincos((double)pos * p.inv_freq[i], &s0, &c0);
+    sincos((double)pos * p.inv_freq[i + 1], &s1, &c1);
+    const float* x = p.A + m * p.lda + p.K + i;
+    float* y = p.rope_out + m * p.H * kDRope + i;
+#pragma unroll 4
+    for (int h = 0; h < p.H; ++h) {
+        const float2 lo = *reinterpret_cast<const float2*>(x + (int64_t)h * p.a_head);
+        const float2 hi = *reinterpret_cast<const float2*>(x + (int64_t)h * p.a_head + 32);
+        float2 ylo, yhi;
+        ylo.x = (float)((double)lo.x * c0 - (double)hi.x * s0);
+        yhi.x = (float)((double)hi.x * c0 + (double)lo.x * s0);
+        ylo.y = (float)((double)lo.y * c1 - (double)hi.y * s1);
+        yhi.y = (float)((double)hi.y * c1 + (double)lo.y * s1);
+        *reinterpret_cast<float2*>(y + (int64_t)h * kDRope) = ylo;
+        *reinterpret_cast<float2*>(y + (int64_t)h * kDRope + 32) = yhi;
     }
 }
 
@@ -138,19 +152,26 @@ template <bool kBTrans>
 __global__ __launch_bounds__(kThreadsProj) void proj_gemm_kernel(ProjArgs p) {
     __shared__ float As[2][kAStage];
     __shared__ float Bs[2][kBStage];
-    const int h = blockIdx.z;
+    // With the rotary step, slice z = 0 rotates (dispatched first, short) and
+    // slice z = 1 + h multiplies head h.
+    int h = blockIdx.z;
+    if (!kBTrans && p.rope_out) {
+        if (h == 0) {
+            if (blockIdx.y * kRopeRows < kBM) rope_rows(p, (int64_t)blockIdx.x * kBM + blockIdx.y * kRopeRows);
+            return;
+        }
+        --h;
+    }
     const int m0 = blockIdx.x * kBM, n0 = blockIdx.y * kBN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 64;
+    const int wm = (wave >> 2) * 32, wn = (wave & 3) * 32;
     const int li = lane & 15, lk = lane >> 4;
 
-    if (!kBTrans && p.rope_out && blockIdx.y == 0) rope_rows(p, h, m0);
-
-    floatx4 acc[2][4];
+    floatx4 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     Stage<kBTrans> st;
     load_stage<kBTrans>(p, h, m0, n0, 0, st);
@@ -164,17 +185,17 @@ __global__ __launch_bounds__(kThreadsProj) void proj_gemm_kernel(ProjArgs p) {
         const float* Bm = Bs[cur];
 #pragma unroll
         for (int kk = 0; kk < kBK; kk += 4) {
-            float a[2], b[4];
+            float a[2], b[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) a[i] = A[(wm + i * 16 + li) * kAStride + kk + lk];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
                 b[j] = kBTrans ? Bm[(wn + j * 16 + li) * kBStrideNK + kk + lk]
                                : Bm[(kk + lk) * kBStrideKN + wn + j * 16 + li];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
         }
         if (s + 1 < n_stage) {
@@ -191,7 +212,7 @@ __global__ __launch_bounds__(kThreadsProj) void proj_gemm_kernel(ProjArgs p) {
             if (m >= p.M) continue;
             float* c = p.C + m * p.ldc + (int64_t)h * p.c_head;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 2; ++j) {
                 const int n = n0 + wn + j * 16 + li;
                 if (n < p.N) c[n] = acc[i][j][r];
             }
@@ -258,7 +279,8 @@ __global__ __launch_bounds__(64) void append_kv_kernel(AppendArgs p) {
 
 
 hipError_t launch_proj(const ProjArgs& p, bool b_trans, hipStream_t stream) {
-    const dim3 grid((unsigned)((p.M + kBM - 1) / kBM), (unsigned)((p.N + kBN - 1) / kBN), (unsigned)p.H);
+    const dim3 grid((unsigned)((p.M + kBM - 1) / kBM), (unsigned)((p.N + kBN - 1) / kBN),
+                    (unsigned)(p.H + (!b_trans && p.rope_out ? 1 : 0)));
     if (b_trans)
         hipLaunchKernelGGL(proj_gemm_kernel<true>, grid, dim3(kThreadsProj), 0, stream, p);
     else
