@@ -60,6 +60,8 @@ def configure(lib):
     lib.ddtvref_tree_accept_row.restype = ctypes.c_int
     lib.ddtvref_compact_rows.argtypes = [P, P, i64, i64, i32, P, i32]
     lib.ddtvref_compact_rows.restype = None
+    lib.ddtvref_fp8_value.argtypes = [ctypes.c_uint8]
+    lib.ddtvref_fp8_value.restype = f64
     lib.ddtvref_rope_neox.argtypes = [P, i32, f64, P]
     lib.ddtvref_rope_neox.restype = None
     lib.ddtvref_tree_positions.argtypes = [P, P, i32, i32, P]
@@ -107,7 +109,12 @@ def build_visibility(parent: np.ndarray):
 
 
 def _kv(a, kv_dtype):
-    return _c(a, np.float32 if kv_dtype == 0 else np.uint16)
+    return _c(a, {0: np.float32, 1: np.uint16, 2: np.uint8}[kv_dtype])
+
+
+def fp8_value(b: int) -> float:
+    """The oracle's decoding of one FP8 E4M3 byte."""
+    return float(_load().ddtvref_fp8_value(int(b)))
 
 
 def verify_attn(q_abs, q_rope, ckv, k_rope, kv_dtype, prefix, bits, scale, rows=None,

@@ -67,9 +67,23 @@ static double bf16_value(uint16_t h)
     return (double)f;
 }
 
+/* An FP8 E4M3 value (the OCP 8-bit floating-point format, "fn" variant): sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 holds the subnormals
+ * m * 2^-9; no infinities; the all-ones magnitude 0x7F is NaN. */
+double ddtvref_fp8_value(uint8_t b)
+{
+    int sign = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m, -9);
+    else v = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
 static double kv_value(const void *base, int kv_dtype, int64_t idx)
 {
     if (kv_dtype == 0) return (double)((const float *)base)[idx];
+    if (kv_dtype == 2) return ddtvref_fp8_value(((const uint8_t *)base)[idx]);
     return bf16_value(((const uint16_t *)base)[idx]);
 }
 
@@ -226,7 +240,7 @@ static void attend_row(const float *q_abs, const float *q_rope, const void *ckv,
 static int check_shapes(int B, int Q, int H, const int32_t *prefix, int kv_dtype)
 {
     if (B < 1 || Q < 1 || H < 1) return REF_EINVAL;
-    if (kv_dtype != 0 && kv_dtype != 1) return REF_EINVAL;
+    if (kv_dtype < 0 || kv_dtype > 2) return REF_EINVAL;
     for (int b = 0; b < B; ++b)
         if (prefix[b] < 0) return REF_EINVAL;
     return REF_OK;
@@ -235,7 +249,8 @@ static int check_shapes(int B, int Q, int H, const int32_t *prefix, int kv_dtype
 /*
  * Attention for a list of query rows.
  *   q_abs  float [B][Q][H][512], q_rope float [B][Q][H][64]
- *   ckv    [sum_b (P_b+Q)][512], k_rope [..][64]; float (kv_dtype 0) or bf16 bits (1)
+ *   ckv    [sum_b (P_b+Q)][512], k_rope [..][64]; float (kv_dtype 0), bf16 bits (1)
+ *          or FP8 E4M3 bytes (2)
  *   prefix int32 [B], bits uint32 [B][Q][W]
  *   rows   flat row ids (b*Q + q)*H + h, n of them; NULL means every row in order
  *   out    double [n][512], lse double [n], psum double [n] (may be NULL)
@@ -299,7 +314,7 @@ int ddtvref_partial(const float *qa, const float *qr, const void *ckv, const voi
                     int kv_dtype, const int64_t *idx, int64_t n, double scale,
                     double *m_out, double *l_out, double *o)
 {
-    if (kv_dtype != 0 && kv_dtype != 1) return REF_EINVAL;
+    if (kv_dtype < 0 || kv_dtype > 2) return REF_EINVAL;
     double *s = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
     double m = -INFINITY;
     for (int64_t k = 0; k < n; ++k) {

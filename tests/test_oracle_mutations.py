@@ -51,6 +51,9 @@ MUTATIONS = [
      "int q = (int)(r % Q);\n        int h = (int)((r / Q) % H);"),
     ("bf16_misread", "uint32_t u = ((uint32_t)h) << 16;", "uint32_t u = ((uint32_t)h) << 15;"),
     ("accept_root_with_parent", "if (i == 0) return par[0] == -1;", "if (i == 0) return 1;"),
+    ("fp8_bias_off_by_one", "else v = ldexp(1.0 + m / 8.0, e - 7);", "else v = ldexp(1.0 + m / 8.0, e - 8);"),
+    ("fp8_subnormal_scale", "if (e == 0) v = ldexp((double)m, -9);", "if (e == 0) v = ldexp((double)m, -10);"),
+    ("fp8_read_as_bf16", "if (kv_dtype == 2) return ddtvref_fp8_value(((const uint8_t *)base)[idx]);", ""),
 ]
 
 PINS = [
@@ -66,6 +69,8 @@ PINS = [
     lambda: pins.test_lse_merge_identity(0),
     pins.test_invalid_trees_reported,
     pins.test_scale_zero_is_mean,
+    pins.test_fp8_decode_every_code,
+    pins.test_fp8_cache_matches_torch,
 ]
 
 

@@ -58,6 +58,8 @@ def bool_to_bits(vis: np.ndarray) -> np.ndarray:
 
 
 def kv_f64(a, kv_dtype):
+    if kv_dtype == wl.FP8:
+        return wl.fp8_bits_to_f32(a).astype(np.float64)
     return (wl.bf16_bits_to_f32(a) if kv_dtype == wl.BF16 else a).astype(np.float64)
 
 
@@ -203,7 +205,7 @@ def test_bf16_widening_exact():
 
 
 # ----------------------------------------------------------------------------- P1 / P2 library routine
-@pytest.mark.parametrize("kv_dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("kv_dtype", [wl.F32, wl.BF16, wl.FP8])
 def test_chain_equals_causal(kv_dtype):
     """A chain tree is causal attention offset by the prefix (the prefill mode)."""
     w = small(B=3, H=4, Q=11, prefix=(0, 7, 40), tree="chain", kv_dtype=kv_dtype)
@@ -355,7 +357,7 @@ def test_scale_zero_is_mean():
                 assert math.isclose(lse[r], math.log(len(idx)), rel_tol=1e-14)
 
 
-@pytest.mark.parametrize("kv_dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("kv_dtype", [wl.F32, wl.BF16, wl.FP8])
 def test_lse_merge_identity(kv_dtype):
     """Attention over V1 u V2 (u V3 empty) equals the log-sum-exp merge of partials."""
     w = small(B=1, H=1, Q=16, prefix=300, tree="best_first", depth_cap=4, kv_dtype=kv_dtype)
@@ -463,3 +465,31 @@ def test_invalid_trees_reported():
     assert vis[3, 1].tolist() == [False, True, False, False]
     assert vis[3, 2].tolist() == [False, False, True, False]
     assert vis[4, 3].tolist() == [False, False, False, True]
+
+
+def test_fp8_decode_every_code():
+    """FP8 E4M3 decoding of all 256 byte values against torch's float8_e4m3fn
+    conversion (a library routine), plus closed forms from the format's definition
+    (bias 7, 3 mantissa bits, subnormals m * 2^-9, 0x7F / 0xFF NaN, no infinities)."""
+    ref = wl.fp8_bits_to_f32(np.arange(256, dtype=np.uint8)).astype(np.float64)
+    got = np.array([oracle.fp8_value(b) for b in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert oracle.fp8_value(0x7E) == 448.0
+    assert oracle.fp8_value(0x08) == 2.0 ** -6
+    assert oracle.fp8_value(0x01) == 2.0 ** -9
+    assert oracle.fp8_value(0x07) == 7 * 2.0 ** -9
+    assert oracle.fp8_value(0x38) == 1.0
+    assert oracle.fp8_value(0xB9) == -1.125
+    assert math.copysign(1.0, oracle.fp8_value(0x80)) == -1.0 and oracle.fp8_value(0x80) == 0.0
+
+
+def test_fp8_cache_matches_torch():
+    """A ragged FP8-cache workload against float64 SDPA over the decoded cache."""
+    w = small(B=3, H=2, Q=12, prefix=(0, 5, 37), tree="best_first", depth_cap=4, kv_dtype=wl.FP8)
+    bits, _, _ = oracle.build_visibility(w.parent)
+    out, lse = oracle.attend_workload(w, bits=bits)
+    ref, rlse = torch_reference(w, np.stack([closure_visibility(p) for p in w.parent]))
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(lse, rlse, rtol=1e-12, atol=1e-12)

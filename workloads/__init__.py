@@ -15,7 +15,9 @@ Recipe (for every workload):
   * numpy PCG64 ``default_rng(seed)``;
   * draw order: trees, prefixes, q_abs, q_rope, ckv, k_rope;
   * float32 tensors are ``standard_normal(dtype=float32) * sigma``;
-  * bf16 tensors are the float32 draw rounded to nearest-even on the bit pattern.
+  * bf16 tensors are the float32 draw rounded to nearest-even on the bit pattern;
+  * FP8 E4M3 tensors are the float32 draw converted by torch's float8_e4m3fn cast
+    (round to nearest even; the draws stay far inside the format's +-448 range).
 """
 from __future__ import annotations
 
@@ -31,6 +33,7 @@ SCALE_192 = 1.0 / math.sqrt(192.0)
 
 F32 = 0
 BF16 = 1
+FP8 = 2      # FP8 E4M3 ("fn": bias 7, no infinities), one byte per value
 
 
 # --------------------------------------------------------------------------- trees
@@ -110,11 +113,34 @@ def round_bf16_bits(x: np.ndarray) -> np.ndarray:
     return (r >> np.uint32(16)).astype(np.uint16)
 
 
-def _normal_rows(rng: np.random.Generator, rows: int, cols: int, sigma: float, bf16: bool,
+def round_fp8_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> FP8 E4M3 bytes (uint8) by torch's float8_e4m3fn conversion."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def fp8_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """FP8 E4M3 bytes -> float32 by torch's conversion (exact)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(b, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).to(torch.float32).numpy()
+
+
+def _normal_rows(rng: np.random.Generator, rows: int, cols: int, sigma: float, bf16,
                  chunk_rows: int = 1 << 16) -> np.ndarray:
-    """rows x cols draws of N(0, sigma^2) as float32 (or bf16 bits), drawn in row
-    chunks: the stream of draws is the same as one big call, but a bf16 result
-    never holds the whole float32 array in memory."""
+    """rows x cols draws of N(0, sigma^2) as float32 (or bf16 bits, or FP8 bytes when
+    bf16 == FP8), drawn in row chunks: the stream of draws is the same as one big
+    call, but a narrow result never holds the whole float32 array in memory."""
+    if not isinstance(bf16, bool) and bf16 == FP8:
+        out8 = np.empty((rows, cols), dtype=np.uint8)
+        for r0 in range(0, rows, chunk_rows):
+            r1 = min(rows, r0 + chunk_rows)
+            a = rng.standard_normal((r1 - r0, cols), dtype=np.float32)
+            if sigma != 1.0:
+                a *= np.float32(sigma)
+            out8[r0:r1] = round_fp8_bits(a)
+        return out8
     if not bf16:
         a = rng.standard_normal((rows, cols), dtype=np.float32)
         if sigma != 1.0:
@@ -145,7 +171,7 @@ class Workload:
     parent: np.ndarray            # int32 [B][Q]
     q_abs: np.ndarray             # float32 [B][Q][H][512]
     q_rope: np.ndarray            # float32 [B][Q][H][64]
-    ckv: np.ndarray               # float32 or uint16(bf16 bits) [sum KV][512]
+    ckv: np.ndarray               # float32, uint16 (bf16 bits) or uint8 (FP8 bytes) [sum KV][512]
     k_rope: np.ndarray            # same dtype [sum KV][64]
     kv_dtype: int                 # F32 or BF16
     scale: float
@@ -209,8 +235,9 @@ def make_workload(name: str, seed: int, B: int, H: int, Q: int, prefix,
     q_rope = rng.standard_normal((B, Q, H, D_ROPE), dtype=np.float32)
     if q_sigma != 1.0:
         q_rope *= np.float32(q_sigma)
-    ckv = _normal_rows(rng, total_kv, D_LATENT, kv_sigma, kv_dtype == BF16)
-    k_rope = _normal_rows(rng, total_kv, D_ROPE, kv_sigma, kv_dtype == BF16)
+    narrow = FP8 if kv_dtype == FP8 else kv_dtype == BF16
+    ckv = _normal_rows(rng, total_kv, D_LATENT, kv_sigma, narrow)
+    k_rope = _normal_rows(rng, total_kv, D_ROPE, kv_sigma, narrow)
     return Workload(name=name, B=B, H=H, Q=Q, prefix=pre, parent=parent.astype(np.int32),
                     q_abs=q_abs, q_rope=q_rope, ckv=ckv, k_rope=k_rope,
                     kv_dtype=kv_dtype, scale=float(scale),
