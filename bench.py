@@ -206,6 +206,40 @@ def time_tail_mode(dd, hip, stream, r, steps=20, warmup=3):
             "us_per_call": round(us, 2), "calls": steps}
 
 
+def time_fp8_cache(dd, hip, stream, r, flops, steps=10, warmup=2):
+    """The same verify call on an FP8 E4M3 copy of the benchmarked cache (a quarter
+    of the fp32 bytes; widened exactly in the kernel): average call time from HIP
+    events and the fp32 matrix-core fraction it reaches."""
+    import torch
+    import workloads as wl
+    from tree_masked_mla_amd.runner import to_device_kv
+    w = r.w
+    if w.kv_dtype != 0:
+        return None
+    ckv8 = to_device_kv(wl.round_fp8_bits(w.ckv), wl.FP8, r.device)
+    kr8 = to_device_kv(wl.round_fp8_bits(w.k_rope), wl.FP8, r.device)
+    need = dd.ddtv_workspace_bytes(r.vis, w.H, wl.FP8)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=r.device)
+
+    def launch():
+        rc = dd.ddtv_verify_attn(r.q_abs, r.q_rope, ckv8, kr8, wl.FP8, w.H, r.vis, w.scale, r.out, r.lse, ws, need,
+                                 stream=stream)
+        assert rc == dd.DDTV_OK, rc
+    for _ in range(warmup):
+        launch()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for _ in range(steps):
+        launch()
+    hip.record(e1, stream)
+    us = hip.elapsed_ms(e0, e1) * 1e3 / steps
+    tf = flops / (us * 1e-6) / 1e12
+    return {"workload": "the same trees and queries over an FP8 E4M3 copy of the cache (widened to fp32 in the kernel)",
+            "cache_bytes": int(ckv8.numel() + kr8.numel()), "us_per_call": round(us, 2),
+            "tflops": round(tf, 2), "frac_of_fp32_mfma_peak": round(tf / PEAK_TFLOPS["f32-mfma"], 4),
+            "tokens_per_s": round(w.B * w.Q / (us * 1e-6), 1), "calls": steps}
+
+
 def time_neighbour(dd, hip, stream, r, d_nope=128, d_v=128, steps=20, warmup=3):
     """The steps around the attention at the benchmarked tree and head counts:
     query preparation (split, rotation, w_kc absorb), the w_vc value projection of
@@ -419,6 +453,7 @@ def main():
     out["tail_mode"] = time_tail_mode(dd, hip, stream, r)
     out["tree_accept"] = time_tree_accept(dd, hip, stream, r)
     out["neighbour"] = time_neighbour(dd, hip, stream, r)
+    out["fp8_cache"] = time_fp8_cache(dd, hip, stream, r, flops)
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(w, budget_s=args.cpu_budget)

@@ -57,7 +57,13 @@ typedef enum {
     DDTV_EDEVICE = 5       /* a HIP call or kernel launch failed */
 } ddtv_status;
 
-typedef enum { DDTV_F32 = 0, DDTV_BF16 = 1 } ddtv_dtype;
+/* Cache element types.  DDTV_FP8_E4M3 is the OCP 8-bit floating-point E4M3 format
+ * ("fn" variant: sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals
+ * m * 2^-9, no infinities, 0x7F / 0xFF NaN; largest finite 448).  Cache values are
+ * used as stored, with no scale: a per-tensor dequantisation scale s folds into
+ * the caller's operands (q_abs * s_ckv and q_rope * s_krope before the call; out
+ * * s_ckv after it). */
+typedef enum { DDTV_F32 = 0, DDTV_BF16 = 1, DDTV_FP8_E4M3 = 2 } ddtv_dtype;
 
 /* Per batch-row cache geometry, kept on the device (16 bytes). */
 typedef struct {
@@ -180,8 +186,9 @@ typedef enum {
     DDTV_PATH_VALU = 1,     /* vector-ALU kernel, fp32 arithmetic (any Q) */
     DDTV_PATH_MFMA = 2,     /* matrix-core kernel in the cache's precision (any Q): fp32 MFMA
                                for fp32 caches; bf16 MFMA with fp32 accumulation for bf16
-                               caches (query and probabilities rounded to bf16) */
-    DDTV_PATH_MFMA_F32 = 3  /* fp32 MFMA for either cache dtype (bf16 widened exactly to
+                               caches (query and probabilities rounded to bf16); FP8 caches
+                               take the fp32 MFMA kernel, widened exactly */
+    DDTV_PATH_MFMA_F32 = 3  /* fp32 MFMA for any cache dtype (bf16 and FP8 widened exactly to
                                fp32): slower on bf16 caches, fp32-accurate */
 } ddtv_path;
 

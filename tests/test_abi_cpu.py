@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert dd.ddtv_version() == 700
+    assert dd.ddtv_version() == 800
     for code in range(6):
         assert dd.ddtv_status_string(code)
     assert dd.ddtv_status_string(2).startswith("malformed tree")
@@ -113,7 +113,7 @@ def test_verify_host_errors(lib):
     assert verify_call(lib, vis, H=0) == E
     assert verify_call(lib, vis, scale=float("nan")) == E
     assert verify_call(lib, vis, scale=float("inf")) == E
-    assert verify_call(lib, vis, kv_dtype=2) == U
+    assert verify_call(lib, vis, kv_dtype=3) == U        # FP8 E4M3 (2) is the last cache dtype
     assert verify_call(lib, vis, opts=dd.make_opts(path=4)) == U
     assert verify_call(lib, vis, opts=dd.make_opts(split_len=100)) == E   # not a multiple of 32
     assert verify_call(lib, vis, opts=dd.make_opts(split_len=-64)) == E

@@ -82,7 +82,7 @@ def test_accept_ties_in_logits():
         assert np.array_equal(got[k], ref[k]), k
 
 
-@pytest.mark.parametrize("kv_dtype", [0, 1])
+@pytest.mark.parametrize("kv_dtype", [0, 1, 2])
 def test_compaction_matches_oracle(kv_dtype):
     """Compaction in place on the device caches: every batch row's rows equal the
     oracle's out-of-place move, and the other batch rows are untouched."""

@@ -131,7 +131,7 @@ def test_path_invariance():
     assert run(w15)[0].plan()[1] == 1    # and VALU below 16 rows
 
 
-@pytest.mark.parametrize("path,kv_dtype", [(1, 0), (2, 0), (2, 1)])
+@pytest.mark.parametrize("path,kv_dtype", [(1, 0), (2, 0), (2, 1), (1, 2), (2, 2)])
 def test_workgroup_order_changes_nothing(path, kv_dtype):
     """The XCD-local and spread work-item orders only change which workgroup
     computes which (batch row, split, query tile): on ragged rows with many
@@ -257,7 +257,8 @@ def _full_sampled(name, n_rows):
     assert np.array_equal(r.bits(), bits)
     assert np.isfinite(out).all() and np.isfinite(lse).all()
     # every row is a convex combination of latent rows: bounded by the cache's extremes
-    kvmax = float(np.abs(wl.bf16_bits_to_f32(w.ckv[:65536]) if w.kv_dtype else w.ckv[:65536]).max())
+    head = w.ckv[:65536]
+    kvmax = float(np.abs({0: lambda a: a, 1: wl.bf16_bits_to_f32, 2: wl.fp8_bits_to_f32}[w.kv_dtype](head)).max())
     assert np.abs(out).max() <= 10 * kvmax
     rows = wl.sample_rows(w, n_rows)
     say(f"oracle {name} on {len(rows)} rows")

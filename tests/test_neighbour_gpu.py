@@ -5,10 +5,10 @@ tree's appended cache rows, and the whole chain parent -> visibility -> append
 
 Bars: float32 results within 1e-4 + 1e-4 |ref| (the fp32 tolerance of the verify
 step); latents copied into the cache bit-exact (float32) or equal to their
-round-to-nearest-even bf16 (bf16 caches); rotated bf16 keys within one bf16 ulp
-of the oracle's value rounded the same way (the rotation's float64 result is
-rounded to float32 first on both sides, so the two can straddle a bf16 tie only
-by float64 rounding noise)."""
+round-to-nearest-even bf16 or FP8 E4M3 codes (narrow caches); rotated narrow keys
+within one code of the oracle's value rounded the same way (the rotation's
+float64 result is rounded to float32 first on both sides, so the two can straddle
+a tie only by float64 rounding noise)."""
 import numpy as np
 import pytest
 
@@ -131,7 +131,7 @@ def test_value_proj_empty_is_a_no_op():
     assert v.item() == 5.0
 
 
-@pytest.mark.parametrize("kv_dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("kv_dtype", [wl.F32, wl.BF16, wl.FP8])
 @pytest.mark.parametrize("explicit", [False, True])
 def test_append_kv_matches_oracle(kv_dtype, explicit):
     import tree_masked_mla_amd as dd
@@ -145,8 +145,10 @@ def test_append_kv_matches_oracle(kv_dtype, explicit):
     rng = np.random.default_rng(43)
     ckv0 = rng.standard_normal((total, 512), dtype=np.float32)
     kr0 = rng.standard_normal((total, 64), dtype=np.float32)
-    if kv_dtype == wl.BF16:
-        ckv0, kr0 = wl.round_bf16_bits(ckv0), wl.round_bf16_bits(kr0)
+    narrow = {wl.BF16: (wl.round_bf16_bits, wl.bf16_bits_to_f32, torch.int16, np.uint16),
+              wl.FP8: (wl.round_fp8_bits, wl.fp8_bits_to_f32, torch.uint8, np.uint8)}.get(kv_dtype)
+    if narrow:
+        ckv0, kr0 = narrow[0](ckv0), narrow[0](kr0)
     ckv = to_device_kv(ckv0, kv_dtype, "cuda")
     kr = to_device_kv(kr0, kv_dtype, "cuda")
     vis, _buf = build_vis(par, prefix)
@@ -155,17 +157,17 @@ def test_append_kv_matches_oracle(kv_dtype, explicit):
                              positions=pos_in) == dd.DDTV_OK
     torch.cuda.synchronize()
     pos = oracle.tree_positions(par, prefix)
-    base_c = wl.bf16_bits_to_f32(ckv0) if kv_dtype == wl.BF16 else ckv0
-    base_k = wl.bf16_bits_to_f32(kr0) if kv_dtype == wl.BF16 else kr0
+    base_c = narrow[1](ckv0) if narrow else ckv0
+    base_k = narrow[1](kr0) if narrow else kr0
     ref_c, ref_k = oracle.append_kv(nb.latent, nb.k_pe, pos, prefix, nb.theta, base_c, base_k)
-    if kv_dtype == wl.BF16:
-        got_c = ckv.view(torch.int16).cpu().numpy().view(np.uint16)
-        got_k = kr.view(torch.int16).cpu().numpy().view(np.uint16)
-        want_c = wl.round_bf16_bits(ref_c.astype(np.float32))
-        assert np.array_equal(got_c, want_c), "latent rows differ from their bf16 rounding"
-        want_k = wl.round_bf16_bits(ref_k.astype(np.float32))
+    if narrow:
+        got_c = ckv.view(narrow[2]).cpu().numpy().view(narrow[3])
+        got_k = kr.view(narrow[2]).cpu().numpy().view(narrow[3])
+        want_c = narrow[0](ref_c.astype(np.float32))
+        assert np.array_equal(got_c, want_c), "latent rows differ from their round-to-nearest-even codes"
+        want_k = narrow[0](ref_k.astype(np.float32))
         ulps = np.abs(got_k.astype(np.int32) - want_k.astype(np.int32))
-        assert ulps.max() <= 1, f"rotated bf16 keys off by {ulps.max()} ulps"
+        assert ulps.max() <= 1, f"rotated keys off by {ulps.max()} ulps"
         owned = np.zeros(total, bool)
         off = 0
         for b in range(B):

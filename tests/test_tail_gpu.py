@@ -57,7 +57,8 @@ def run_tail(w, split_len=0, want_lse=True):
     return r, out, lse
 
 
-@pytest.mark.parametrize("kv_dtype,split_len,want_lse", [(0, 0, True), (1, 0, True), (0, 32, True), (0, 0, False)])
+@pytest.mark.parametrize("kv_dtype,split_len,want_lse", [(0, 0, True), (1, 0, True), (2, 0, True), (0, 32, True),
+                                                                (0, 0, False)])
 def test_tail_mode_equals_full_attention(kv_dtype, split_len, want_lse):
     w = wl.make_workload("tail", 3300 + kv_dtype, B=3, H=8, Q=24, prefix=[0, 500, 1300], tree="uniform",
                          kv_dtype=kv_dtype)

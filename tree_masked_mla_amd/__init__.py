@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libddtv.so")
 
 DDTV_OK, DDTV_EINVAL, DDTV_ETREE, DDTV_EUNSUPPORTED, DDTV_EWORKSPACE, DDTV_EDEVICE = range(6)
-DDTV_F32, DDTV_BF16 = 0, 1
+DDTV_F32, DDTV_BF16, DDTV_FP8_E4M3 = 0, 1, 2
 DDTV_PATH_AUTO, DDTV_PATH_VALU, DDTV_PATH_MFMA, DDTV_PATH_MFMA_F32 = 0, 1, 2, 3
 DDTV_ORDER_AUTO, DDTV_ORDER_XCD_LOCAL, DDTV_ORDER_SPREAD = 0, 1, 2
 D_LATENT, D_ROPE, MAX_Q = 512, 64, 256

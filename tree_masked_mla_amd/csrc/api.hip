@@ -20,7 +20,7 @@ using namespace ddtv;
 
 namespace {
 
-constexpr int32_t kVersion = 700;   // 0.7.0: query preparation, value projection, appended cache rows
+constexpr int32_t kVersion = 800;   // 0.8.0: FP8 E4M3 caches
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -66,6 +66,8 @@ int cu_count() {
 
 constexpr int32_t kMaxProjHeads = 1024;          // heads per projection call (grid z)
 constexpr int64_t kMaxProjRows = (int64_t)1 << 30; // tokens per projection call (grid x * 256 threads < 2^32)
+
+bool dtype_ok(int d) { return d == DDTV_F32 || d == DDTV_BF16 || d == DDTV_FP8_E4M3; }
 
 bool rope_ok(double theta) { return std::isfinite(theta) && theta > 0.0; }
 
@@ -205,7 +207,7 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     ddtv_status st = check_vis(vis);
     if (st) return st;
     if (H < 1 || H > 65536) return DDTV_EINVAL;
-    if (kv_dtype != DDTV_F32 && kv_dtype != DDTV_BF16) return DDTV_EUNSUPPORTED;
+    if (!dtype_ok(kv_dtype)) return DDTV_EUNSUPPORTED;
     const int path_req = opts ? opts->path : DDTV_PATH_AUTO;
     if (path_req != DDTV_PATH_AUTO && path_req != DDTV_PATH_VALU && path_req != DDTV_PATH_MFMA &&
         path_req != DDTV_PATH_MFMA_F32)
@@ -222,7 +224,8 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     // cases with fewer rows than that.
     p->path = path_req != DDTV_PATH_AUTO ? path_req
                                          : ((int64_t)vis->Q * H < kValuRows ? DDTV_PATH_VALU : DDTV_PATH_MFMA);
-    if (p->path == DDTV_PATH_MFMA_F32 && kv_dtype == DDTV_F32) p->path = DDTV_PATH_MFMA;
+    // fp32 and FP8 caches run the fp32 matrix-core kernel under either matrix path
+    if (p->path == DDTV_PATH_MFMA_F32 && kv_dtype != DDTV_BF16) p->path = DDTV_PATH_MFMA;
     p->bf16_mma = p->path == DDTV_PATH_MFMA && kv_dtype == DDTV_BF16;
     p->rows_per_wg = p->path == DDTV_PATH_VALU ? kValuRows : (p->bf16_mma ? bf16_rows_per_workgroup() : mfma_rows_per_workgroup(kv_dtype));
     const int64_t R = (int64_t)vis->Q * H;
@@ -493,7 +496,7 @@ ddtv_status ddtv_tree_accept(const float* logits, int32_t V, const int32_t* pare
     if ((ckv == nullptr) != (k_rope == nullptr)) return DDTV_EINVAL;
     if (ckv) {
         if (!aligned(ckv, 16) || !aligned(k_rope, 16)) return DDTV_EINVAL;
-        if (kv_dtype != DDTV_F32 && kv_dtype != DDTV_BF16) return DDTV_EUNSUPPORTED;
+        if (!dtype_ok(kv_dtype)) return DDTV_EUNSUPPORTED;
     }
     if ((int64_t)vis->B * vis->Q > (int64_t)UINT32_MAX) return DDTV_EUNSUPPORTED;
     AcceptArgs a;
@@ -507,7 +510,7 @@ ddtv_status ddtv_tree_accept(const float* logits, int32_t V, const int32_t* pare
     a.accept_len = accept_len;
     a.ckv = ckv;
     a.k_rope = k_rope;
-    a.kv_elem = kv_dtype == DDTV_BF16 ? 2 : 4;
+    a.kv_elem = kv_dtype == DDTV_F32 ? 4 : (kv_dtype == DDTV_BF16 ? 2 : 1);
     a.B = vis->B;
     a.Q = vis->Q;
     a.V = V;
@@ -674,7 +677,7 @@ ddtv_status ddtv_append_kv(const float* latent, const float* k_pe, const ddtv_vi
     ddtv_status st = check_vis(vis);
     if (st) return st;
     if (!rope_ok(rope_theta)) return DDTV_EINVAL;
-    if (kv_dtype != DDTV_F32 && kv_dtype != DDTV_BF16) return DDTV_EUNSUPPORTED;
+    if (!dtype_ok(kv_dtype)) return DDTV_EUNSUPPORTED;
     if ((int64_t)vis->B * vis->Q > (int64_t)INT32_MAX) return DDTV_EUNSUPPORTED;
     AppendArgs p{};
     p.latent = latent;
@@ -687,7 +690,7 @@ ddtv_status ddtv_append_kv(const float* latent, const float* k_pe, const ddtv_vi
     p.B = vis->B;
     p.Q = vis->Q;
     p.W = vis->W;
-    p.bf16 = kv_dtype == DDTV_BF16;
+    p.dtype = kv_dtype;
     rope_frequencies(rope_theta, p.inv_freq);
     return launch_append_kv(p, stream) == hipSuccess ? DDTV_OK : DDTV_EDEVICE;
 }

@@ -30,7 +30,8 @@
 //  * Online softmax in exp2 units with lazy rescaling (the running max moves only
 //    when a tile beats it by more than 2^8).
 //  * fp32 caches go HBM->LDS with global_load_lds_dwordx4 (no VGPR staging),
-//    double buffered; bf16 caches are widened to fp32 through VGPRs on the way in.
+//    double buffered; bf16 and FP8 caches are widened exactly to fp32 through
+//    VGPRs on the way in.
 #include "ddtv_internal.hpp"
 
 namespace ddtv {
@@ -89,12 +90,12 @@ __device__ __forceinline__ void issue_tile_f32(f32x4* buf, const AttnArgs& a, in
     }
 }
 
-// bf16 cache: 16-byte loads (8 values) into VGPRs ...
-struct Bf16Stage {
+// bf16 and FP8 caches: 16-byte loads (8 or 16 values) into VGPRs ...
+struct NarrowStage {
     uint4 v[5];
 };
 
-__device__ __forceinline__ void load_tile_bf16(Bf16Stage& st, const AttnArgs& a, int64_t kv_base, int t0,
+__device__ __forceinline__ void load_tile_bf16(NarrowStage& st, const AttnArgs& a, int64_t kv_base, int t0,
                                                int kv_last, int tid) {
     const uint4* ck = reinterpret_cast<const uint4*>(a.ckv);
     const uint4* kr = reinterpret_cast<const uint4*>(a.k_rope);
@@ -110,7 +111,7 @@ __device__ __forceinline__ void load_tile_bf16(Bf16Stage& st, const AttnArgs& a,
 }
 
 // ... then widened and written to the swizzled fp32 layout.
-__device__ __forceinline__ void store_tile_bf16(f32x4* buf, const Bf16Stage& st, int tid) {
+__device__ __forceinline__ void store_tile_bf16(f32x4* buf, const NarrowStage& st, int tid) {
 #pragma unroll
     for (int k = 0; k < 5; ++k) {
         if (k == 4 && tid >= 256) break;
@@ -127,6 +128,64 @@ __device__ __forceinline__ void store_tile_bf16(f32x4* buf, const Bf16Stage& st,
             buf[rope_at(r, 2 * c + 1)] = hi;
         }
     }
+}
+
+// FP8: a tile is 32 rows x 32 latent pieces + 32 rows x 4 rope pieces of 16 bytes.
+__device__ __forceinline__ void load_tile_fp8(NarrowStage& st, const AttnArgs& a, int64_t kv_base, int t0,
+                                              int kv_last, int tid) {
+    const uint4* ck = reinterpret_cast<const uint4*>(a.ckv);
+    const uint4* kr = reinterpret_cast<const uint4*>(a.k_rope);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int r = k * 16 + (tid >> 5), c = tid & 31;
+        st.v[k] = ck[(kv_base + min(t0 + r, kv_last)) * 32 + c];
+    }
+    if (tid < 128) {
+        const int r = tid >> 2, c = tid & 3;
+        st.v[2] = kr[(kv_base + min(t0 + r, kv_last)) * 4 + c];
+    }
+}
+
+__device__ __forceinline__ f32x4 fp8_chunk(uint32_t w) {
+    const float4 f = fp8x4(w);
+    return f32x4{f.x, f.y, f.z, f.w};
+}
+
+__device__ __forceinline__ void store_tile_fp8(f32x4* buf, const NarrowStage& st, int tid) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int r = k * 16 + (tid >> 5), c = tid & 31;
+        const uint4 v = st.v[k];
+        buf[lat_at(r, 4 * c)] = fp8_chunk(v.x);
+        buf[lat_at(r, 4 * c + 1)] = fp8_chunk(v.y);
+        buf[lat_at(r, 4 * c + 2)] = fp8_chunk(v.z);
+        buf[lat_at(r, 4 * c + 3)] = fp8_chunk(v.w);
+    }
+    if (tid < 128) {
+        const int r = tid >> 2, c = tid & 3;
+        const uint4 v = st.v[2];
+        buf[rope_at(r, 4 * c)] = fp8_chunk(v.x);
+        buf[rope_at(r, 4 * c + 1)] = fp8_chunk(v.y);
+        buf[rope_at(r, 4 * c + 2)] = fp8_chunk(v.z);
+        buf[rope_at(r, 4 * c + 3)] = fp8_chunk(v.w);
+    }
+}
+
+// One tile of a narrow (bf16 or FP8) cache: load into VGPRs, then widen into LDS.
+template <int KV>
+__device__ __forceinline__ void load_tile_narrow(NarrowStage& st, const AttnArgs& a, int64_t kv_base, int t0,
+                                                 int kv_last, int tid) {
+    if (KV == DDTV_FP8_E4M3)
+        load_tile_fp8(st, a, kv_base, t0, kv_last, tid);
+    else
+        load_tile_bf16(st, a, kv_base, t0, kv_last, tid);
+}
+template <int KV>
+__device__ __forceinline__ void store_tile_narrow(f32x4* buf, const NarrowStage& st, int tid) {
+    if (KV == DDTV_FP8_E4M3)
+        store_tile_fp8(buf, st, tid);
+    else
+        store_tile_bf16(buf, st, tid);
 }
 
 struct Smem {
@@ -270,7 +329,7 @@ __device__ __forceinline__ void sm_pv_slot(f32x4 (&oacc)[16], const f32x4* sx_mi
 }
 
 // One workgroup's work; HALF is the wave's half of the pair (wave-uniform).
-template <int KV_BF16, int HALF>
+template <int KV, int HALF>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, int s, int rt, int wave,
                                           int lane) {
     const int tid = wave * 64 + lane;
@@ -286,11 +345,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
     const int ntiles = (kv_hi - kv_lo + kTile - 1) / kTile;
     const int64_t kv_base = rowd.kv_off;
 
-    Bf16Stage stage;
-    if (!KV_BF16)
+    NarrowStage stage;
+    if (KV == DDTV_F32)
         issue_tile_f32(sm.kv[0], a, kv_base, kv_lo, kv_len - 1, wave, lane);
     else
-        load_tile_bf16(stage, a, kv_base, kv_lo, kv_len - 1, tid);
+        load_tile_narrow<KV>(stage, a, kv_base, kv_lo, kv_len - 1, tid);
 
     // Query half: register t holds dims 16(18*HALF + t) + 4g .. +3 of row n (this
     // permutation of the contraction index matches the cache-operand reads),
@@ -317,7 +376,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
     float m_run = -INFINITY;   // running max of row n (exp2 units)
     float l_lane = 0.f;        // this lane's share of the running sum of row n
 
-    if (KV_BF16) store_tile_bf16(sm.kv[0], stage, tid);
+    if (KV != DDTV_F32) store_tile_narrow<KV>(sm.kv[0], stage, tid);
 
     const TileOffsets to = tile_offsets(g, n);
     f32x4* sx_mine = &sm.sx[wave][0][0];
@@ -332,13 +391,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
             __syncthreads();
             const bool more = it + 1 < ntiles;
             if (more) {
-                if (!KV_BF16)
+                if (KV == DDTV_F32)
                     issue_tile_f32(sm.kv[(it + 1) & 1], a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, wave, lane);
                 else
-                    load_tile_bf16(stage, a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, tid);
+                    load_tile_narrow<KV>(stage, a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, tid);
             }
             __syncthreads();
-            if (KV_BF16 && more) store_tile_bf16(sm.kv[(it + 1) & 1], stage, tid);
+            if (KV != DDTV_F32 && more) store_tile_narrow<KV>(sm.kv[(it + 1) & 1], stage, tid);
         }
         return;   // no rows to write
     }
@@ -348,10 +407,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         const bool more = it + 1 < ntiles;
         auto issue = [&]() {
             if (more) {
-                if (!KV_BF16)
+                if (KV == DDTV_F32)
                     issue_tile_f32(sm.kv[(it + 1) & 1], a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, wave, lane);
                 else
-                    load_tile_bf16(stage, a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, tid);
+                    load_tile_narrow<KV>(stage, a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, tid);
             }
         };
         const char* Kb = reinterpret_cast<const char*>(sm.kv[it & 1]);
@@ -359,7 +418,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         __syncthreads();                                  // partner's partial scores are in LDS
         sm_pv_slot<HALF>(oacc, sx_mine, sx_partner, Kb, to, m_run, l_lane, mrow, g, n, lane, kv_lo + it * kTile, P,
                          kv_hi);
-        if (KV_BF16 && more) store_tile_bf16(sm.kv[(it + 1) & 1], stage, tid);
+        if (KV != DDTV_F32 && more) store_tile_narrow<KV>(sm.kv[(it + 1) & 1], stage, tid);
     }
 
     // ---- epilogue: output rows pair*16 + 4g + j of the tile, dims 256*HALF + 64T + 4n + (0..3)
@@ -400,7 +459,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
     }
 }
 
-template <int KV_BF16>
+template <int KV>
 __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs a) {
     __shared__ Smem sm;
     const int64_t w = work_item(a);
@@ -412,9 +471,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (wave & 1)
-        attn_body<KV_BF16, 1>(a, sm, b, s, rt, wave, lane);
+        attn_body<KV, 1>(a, sm, b, s, rt, wave, lane);
     else
-        attn_body<KV_BF16, 0>(a, sm, b, s, rt, wave, lane);
+        attn_body<KV, 0>(a, sm, b, s, rt, wave, lane);
 }
 
 }  // namespace
@@ -424,9 +483,11 @@ int mfma_rows_per_workgroup(int /*kv_dtype*/) { return kRows; }
 hipError_t launch_attn_mfma(const AttnArgs& a, int kv_dtype, int64_t grid, hipStream_t stream) {
     (void)hipGetLastError();   // report only this launch's error
     if (kv_dtype == DDTV_BF16)
-        hipLaunchKernelGGL(attn_mfma_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(attn_mfma_kernel<DDTV_BF16>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    else if (kv_dtype == DDTV_FP8_E4M3)
+        hipLaunchKernelGGL(attn_mfma_kernel<DDTV_FP8_E4M3>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL(attn_mfma_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(attn_mfma_kernel<DDTV_F32>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

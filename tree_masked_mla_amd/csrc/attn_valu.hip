@@ -24,16 +24,30 @@ constexpr int kRows = kValuRows;            // 16
 constexpr int kChunks = kDQK / 4;           // 144 float4 per cache row
 constexpr int kStride = kChunks + 1;        // padded LDS row (580 floats)
 
-template <int KV_BF16>
+template <int KV>
 __device__ __forceinline__ void load_kv_tile(float4 (*skv)[kStride], const AttnArgs& a, int64_t kv_base,
                                              int t0, int kv_last, int tid) {
-    if (!KV_BF16) {
+    if (KV == DDTV_F32) {
         const float4* ck = reinterpret_cast<const float4*>(a.ckv);
         const float4* kr = reinterpret_cast<const float4*>(a.k_rope);
         for (int idx = tid; idx < kTile * kChunks; idx += 256) {
             const int r = idx / kChunks, c = idx - r * kChunks;
             const int64_t row = kv_base + min(t0 + r, kv_last);
             skv[r][c] = (c < 128) ? ck[row * 128 + c] : kr[row * 16 + (c - 128)];
+        }
+    } else if (KV == DDTV_FP8_E4M3) {
+        // 16 FP8 values (16 bytes) per load -> four float4 chunks
+        const uint4* ck = reinterpret_cast<const uint4*>(a.ckv);
+        const uint4* kr = reinterpret_cast<const uint4*>(a.k_rope);
+        constexpr int kB8 = kChunks / 4;    // 36 x 16 B per row
+        for (int idx = tid; idx < kTile * kB8; idx += 256) {
+            const int r = idx / kB8, c = idx - r * kB8;
+            const int64_t row = kv_base + min(t0 + r, kv_last);
+            const uint4 v = (c < 32) ? ck[row * 32 + c] : kr[row * 4 + (c - 32)];
+            skv[r][4 * c] = fp8x4(v.x);
+            skv[r][4 * c + 1] = fp8x4(v.y);
+            skv[r][4 * c + 2] = fp8x4(v.z);
+            skv[r][4 * c + 3] = fp8x4(v.w);
         }
     } else {
         // 8 bf16 (16 bytes) per load -> two float4 chunks
@@ -50,7 +64,7 @@ __device__ __forceinline__ void load_kv_tile(float4 (*skv)[kStride], const AttnA
     }
 }
 
-template <int KV_BF16>
+template <int KV>
 __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
     __shared__ float4 sq[kRows][kChunks];     // 36 KiB: the workgroup's query rows
     __shared__ float4 skv[kTile][kStride];    // 72.5 KiB: one cache tile
@@ -102,7 +116,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 
     for (int t0 = kv_lo; t0 < kv_hi; t0 += kTile) {
         __syncthreads();   // previous tile fully consumed (and staging above visible)
-        load_kv_tile<KV_BF16>(skv, a, rowd.kv_off, t0, kv_len - 1, tid);
+        load_kv_tile<KV>(skv, a, rowd.kv_off, t0, kv_len - 1, tid);
         __syncthreads();
 
         // scores of cache row t0 + kvl against the wave's 4 query rows
@@ -191,9 +205,11 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 hipError_t launch_attn_valu(const AttnArgs& a, int kv_dtype, int64_t grid, hipStream_t stream) {
     (void)hipGetLastError();   // report only this launch's error
     if (kv_dtype == DDTV_BF16)
-        hipLaunchKernelGGL(attn_valu_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(attn_valu_kernel<DDTV_BF16>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    else if (kv_dtype == DDTV_FP8_E4M3)
+        hipLaunchKernelGGL(attn_valu_kernel<DDTV_FP8_E4M3>, dim3((unsigned)grid), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL(attn_valu_kernel<0>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(attn_valu_kernel<DDTV_F32>, dim3((unsigned)grid), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -226,6 +226,39 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
     return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Float32 -> FP8 E4M3 ("fn") byte, round to nearest, ties to even; magnitudes
+// above 464 (which round past the largest finite value, 448) saturate to 448.
+//  - normal results (|x| >= 2^-6): the float32 exponent/mantissa fields are
+//    rounded to 3 mantissa bits by adding half an fp8 ulp minus one plus the
+//    kept lsb, then rebased (bias 127 -> 7); a carry out of the mantissa moves
+//    into the exponent, as it should;
+//  - subnormal results: round |x| * 2^9 to an integer (0..8; 8 is the smallest
+//    normal, 0x08, so the code is that integer either way).
+__device__ __forceinline__ uint32_t to_fp8(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    uint32_t code;
+    if (a > 0x43e80000u) {                       // > 464
+        code = 0x7eu;
+    } else if (a >= 0x3c800000u) {               // >= 2^-6
+        const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+        code = (r >> 20) - (120u << 3);
+    } else {
+        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+    }
+    return sign | code;
+}
+
+__device__ __forceinline__ void store_cache(void* base, int dtype, int64_t idx, float v) {
+    if (dtype == DDTV_BF16)
+        reinterpret_cast<uint16_t*>(base)[idx] = to_bf16(v);
+    else if (dtype == DDTV_FP8_E4M3)
+        reinterpret_cast<uint8_t*>(base)[idx] = (uint8_t)to_fp8(v);
+    else
+        reinterpret_cast<float*>(base)[idx] = v;
+}
+
 // One wave per tree node: its latent row and its rotated rope key go to cache
 // row kv_off + prefix + node.
 __global__ __launch_bounds__(64) void append_kv_kernel(AppendArgs p) {
@@ -248,11 +281,14 @@ __global__ __launch_bounds__(64) void append_kv_kernel(AppendArgs p) {
     for (int u = 0; u < 2; ++u) {
         const int c = (lane + u * 64) * 4;
         const float4 v = ld4(lat + c);
-        if (p.bf16) {
+        if (p.dtype == DDTV_BF16) {
             uint16_t* d = reinterpret_cast<uint16_t*>(p.ckv) + r * kDLat + c;
             ushort4 o;
             o.x = to_bf16(v.x); o.y = to_bf16(v.y); o.z = to_bf16(v.z); o.w = to_bf16(v.w);
             *reinterpret_cast<ushort4*>(d) = o;
+        } else if (p.dtype == DDTV_FP8_E4M3) {
+            uint32_t* d = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.ckv) + r * kDLat + c);
+            *d = to_fp8(v.x) | (to_fp8(v.y) << 8) | (to_fp8(v.z) << 16) | (to_fp8(v.w) << 24);
         } else {
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.ckv) + r * kDLat + c) = v;
         }
@@ -263,15 +299,8 @@ __global__ __launch_bounds__(64) void append_kv_kernel(AppendArgs p) {
         double sn, cs;
         sincos((double)pos * p.inv_freq[lane], &sn, &cs);
         const float y0 = (float)(x0 * cs - x1 * sn), y1 = (float)(x1 * cs + x0 * sn);
-        if (p.bf16) {
-            uint16_t* d = reinterpret_cast<uint16_t*>(p.k_rope) + r * kDRope;
-            d[lane] = to_bf16(y0);
-            d[lane + 32] = to_bf16(y1);
-        } else {
-            float* d = reinterpret_cast<float*>(p.k_rope) + r * kDRope;
-            d[lane] = y0;
-            d[lane + 32] = y1;
-        }
+        store_cache(p.k_rope, p.dtype, r * kDRope + lane, y0);
+        store_cache(p.k_rope, p.dtype, r * kDRope + lane + 32, y1);
     }
 }
 

@@ -36,7 +36,8 @@ struct AppendArgs {
     const ddtv_row* rows;       // [B]
     void* ckv;                  // [total_kv][512] f32 or bf16
     void* k_rope;               // [total_kv][64]
-    int B, Q, W, bf16;
+    int B, Q, W;
+    int dtype;                  // ddtv_dtype of the caches
     double inv_freq[32];
 };
 

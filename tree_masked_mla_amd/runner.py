@@ -7,12 +7,14 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (DDTV_BF16, DDTV_ORDER_AUTO, DDTV_PATH_AUTO, check, ddtv_build_visibility, ddtv_plan_info, ddtv_vis_bytes,
+from . import (DDTV_BF16, DDTV_FP8_E4M3, DDTV_ORDER_AUTO, DDTV_PATH_AUTO, check, ddtv_build_visibility, ddtv_plan_info, ddtv_vis_bytes,
                ddtv_verify_attn, ddtv_workspace_bytes, load, make_opts)
 
 
 def to_device_kv(a: np.ndarray, kv_dtype: int, device) -> torch.Tensor:
-    """float32 array, or bf16 bit patterns (uint16), to a device tensor."""
+    """float32 array, bf16 bit patterns (uint16) or FP8 E4M3 bytes (uint8), to a device tensor."""
+    if kv_dtype == DDTV_FP8_E4M3:
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(device)
     if kv_dtype == DDTV_BF16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
