@@ -182,28 +182,38 @@ def time_tree_accept(dd, hip, stream, r, V=32768, steps=20, warmup=3):
 def time_tail_mode(dd, hip, stream, r, steps=20, warmup=3):
     """External-prefix mode on the benchmarked workload: the tree rows only, merged
     with a prefix result supplied by the caller (here any normalised rows and
-    finite lse: timing only); average call time from HIP events."""
+    finite lse: timing only); average call time from HIP events, for the default
+    tree-sparse route and for the dense route (forced matrix-core path)."""
     import torch
     w = r.w
     po = torch.zeros_like(r.out)
     pl = torch.zeros((w.B, w.Q, w.H), dtype=torch.float32, device=r.device)
     need = dd.ddtv_tail_workspace_bytes(r.vis, w.H, w.kv_dtype)
+    dense = dd.make_opts(path=dd.DDTV_PATH_MFMA)
+    need = max(need, dd.ddtv_tail_workspace_bytes(r.vis, w.H, w.kv_dtype, dense))
     ws = torch.empty(need, dtype=torch.uint8, device=r.device)
 
-    def launch():
-        rc = dd.ddtv_verify_attn_tail(r.q_abs, r.q_rope, r.ckv, r.k_rope, w.kv_dtype, w.H, r.vis, w.scale, po, pl,
-                                      r.out, r.lse, ws, stream=stream)
-        assert rc == dd.DDTV_OK, rc
-    for _ in range(warmup):
-        launch()
-    e0, e1 = hip.event(), hip.event()
-    hip.record(e0, stream)
-    for _ in range(steps):
-        launch()
-    hip.record(e1, stream)
-    us = hip.elapsed_ms(e0, e1) * 1e3 / steps
+    def timed(opts):
+        def launch():
+            rc = dd.ddtv_verify_attn_tail(r.q_abs, r.q_rope, r.ckv, r.k_rope, w.kv_dtype, w.H, r.vis, w.scale, po,
+                                          pl, r.out, r.lse, ws, stream=stream, opts=opts)
+            assert rc == dd.DDTV_OK, rc
+        for _ in range(warmup):
+            launch()
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, stream)
+        for _ in range(steps):
+            launch()
+        hip.record(e1, stream)
+        return hip.elapsed_ms(e0, e1) * 1e3 / steps
+
+    us = timed(None)
+    us_dense = timed(dense)
+    nbytes = 4 * w.B * w.Q * w.H * (512 + 64 + 512 + 1 + 512 + 1)   # q, prefix result in, out + lse
     return {"workload": f"the same trees, tree rows only ({w.Q} per batch row) + merge with a caller's prefix result",
-            "us_per_call": round(us, 2), "calls": steps}
+            "us_per_call": round(us, 2), "route": "tree-sparse (each node visits its ancestors-or-self)",
+            "streamed_bytes": nbytes, "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "dense_route_us_per_call": round(us_dense, 2), "calls": steps}
 
 
 def time_fp8_cache(dd, hip, stream, r, flops, steps=10, warmup=2):

@@ -273,7 +273,12 @@ ddtv_status ddtv_verify_attn_ex(const float *q_abs, const float *q_rope, const v
  *   other arguments as for ddtv_verify_attn_ex; out/lse receive the merged result,
  *   which equals ddtv_verify_attn over prefix and tree when the prefix result is
  *   exact.  workspace: at least ddtv_tail_workspace_bytes(), 256-byte aligned
- *   (never NULL: it also holds a row table and the tree rows' lse).
+ *   (never NULL: the dense route keeps a row table and the tree rows' lse there).
+ * Routes: with opts NULL, or path AUTO and split_len 0, one launch visits for
+ * each node only its ancestors-or-self (fp32 arithmetic on any cache dtype,
+ * cache values widened exactly) and merges the prefix result in the same pass;
+ * a forced path or split length runs the attention kernels of ddtv_verify_attn_ex
+ * over the tree rows, then a merge launch.
  * Errors: as ddtv_verify_attn_ex, plus DDTV_EINVAL for a null or misaligned prefix
  * result.
  */

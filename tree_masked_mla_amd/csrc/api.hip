@@ -470,6 +470,35 @@ ddtv_status ddtv_verify_attn_tail(const float* q_abs, const float* q_rope, const
     if (st) return st;
     if (!workspace || workspace_bytes < L.total) return DDTV_EWORKSPACE;
     if (!aligned(workspace, 256)) return DDTV_EINVAL;
+    if (!opts || (opts->path == DDTV_PATH_AUTO && opts->split_len == 0)) {
+        // tree-sparse route: each node visits only its ancestors-or-self
+        if (!q_abs || !q_rope || !ckv || !k_rope) return DDTV_EINVAL;
+        if (!aligned(q_abs, 16) || !aligned(q_rope, 16) || !aligned(ckv, 16) || !aligned(k_rope, 16) ||
+            !aligned(out, 16) || (lse && !aligned(lse, 4)))
+            return DDTV_EINVAL;
+        if (!std::isfinite(scale)) return DDTV_EINVAL;
+        if ((int64_t)vis->B * vis->Q > (int64_t)INT32_MAX) return DDTV_EUNSUPPORTED;
+        TailSparseArgs a;
+        a.q_abs = q_abs;
+        a.q_rope = q_rope;
+        a.ckv = ckv;
+        a.k_rope = k_rope;
+        a.bits = vis->bits;
+        a.rows = vis->rows;
+        a.prefix_out = prefix_out;
+        a.prefix_lse = prefix_lse;
+        a.out = out;
+        a.lse = lse;
+        a.B = vis->B;
+        a.Q = vis->Q;
+        a.H = H;
+        a.W = vis->W;
+        a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+        if (opts && opts->attn_begin && hipEventRecord(opts->attn_begin, stream) != hipSuccess) return DDTV_EDEVICE;
+        if (launch_tail_sparse(a, kv_dtype, stream) != hipSuccess) return DDTV_EDEVICE;
+        if (opts && opts->attn_end && hipEventRecord(opts->attn_end, stream) != hipSuccess) return DDTV_EDEVICE;
+        return DDTV_OK;
+    }
     char* ws = static_cast<char*>(workspace);
     ddtv_row* rows = reinterpret_cast<ddtv_row*>(ws + L.rows);
     float* lse_tail = reinterpret_cast<float*>(ws + L.lse);

@@ -15,4 +15,24 @@ hipError_t launch_tail_rows(const ddtv_row* rows, ddtv_row* tail_rows, int B, in
 hipError_t launch_tail_merge(float* out, const float* lse_tail, float* lse, const float* prefix_out,
                              const float* prefix_lse, int64_t n, hipStream_t stream);
 
+// Everything the tree-sparse tail kernel needs (passed by value).
+struct TailSparseArgs {
+    const float* q_abs;         // [B][Q][H][512]
+    const float* q_rope;        // [B][Q][H][64]
+    const void* ckv;            // [total_kv][512] of the cache dtype
+    const void* k_rope;         // [total_kv][64]
+    const uint32_t* bits;       // [B][Q][W]
+    const ddtv_row* rows;       // [B]
+    const float* prefix_out;    // [B][Q][H][512], normalised
+    const float* prefix_lse;    // [B][Q][H], natural log
+    float* out;                 // [B][Q][H][512]
+    float* lse;                 // [B][Q][H] or null
+    int B, Q, H, W;
+    float scale_log2;           // scale * log2(e)
+};
+
+// Attention of every tree node over its own ancestors-or-self only, merged with
+// the caller's prefix result, in one launch (one workgroup per node).
+hipError_t launch_tail_sparse(const TailSparseArgs& a, int kv_dtype, hipStream_t stream);
+
 }  // namespace ddtv
