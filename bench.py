@@ -216,6 +216,63 @@ def time_tail_mode(dd, hip, stream, r, steps=20, warmup=3):
             "dense_route_us_per_call": round(us_dense, 2), "calls": steps}
 
 
+def time_iteration(dd, hip, stream, r, V=32768, D=12, K=4, steps=10, warmup=2):
+    """One whole tree-verify iteration on the device at the benchmarked batch, tree
+    size and cache: draft-tree builder -> visibility -> the tree's cache rows ->
+    query preparation -> attention (S2..S7) -> value projection -> greedy
+    acceptance with compaction.  Synthetic drafter top-K, projections, weights and
+    target logits; the resident cache; average iteration time from HIP events."""
+    import torch
+    import workloads as wl
+    w = r.w
+    B, Q, H, dev = w.B, w.Q, w.H, r.device
+    lp, tok = wl.drafter_topk(7400 + B + Q, B, D, K)
+    lp_d, tok_d = torch.from_numpy(lp).to(dev), torch.from_numpy(tok).to(dev)
+    nb = wl.neighbour_inputs(7500 + B + Q, B, Q, H)
+    q, w_kc, w_vc = (torch.from_numpy(x).to(dev) for x in (nb.q, nb.w_kc, nb.w_vc))
+    lat, k_pe = torch.from_numpy(nb.latent).to(dev), torch.from_numpy(nb.k_pe).to(dev)
+    logits = torch.from_numpy(wl.target_logits(7600 + B + Q, B, Q, V)).to(dev)
+    i32 = lambda *shape: torch.empty(shape, dtype=torch.int32, device=dev)
+    parent, token, pred, path, out_tok, alen = i32(B, Q), i32(B, Q), i32(B, Q), i32(B, Q), i32(B, Q), i32(B)
+    q_abs = torch.empty((B, Q, H, 512), dtype=torch.float32, device=dev)
+    q_rope = torch.empty((B, Q, H, 64), dtype=torch.float32, device=dev)
+    v = torch.empty((B, Q, H, 128), dtype=torch.float32, device=dev)
+    vis_buf = torch.empty(dd.ddtv_vis_bytes(B, Q), dtype=torch.uint8, device=dev)
+    prefix = np.ascontiguousarray(w.prefix, dtype=np.int32)
+    state = {}
+
+    def iteration():
+        ok = dd.DDTV_OK
+        assert dd.ddtv_build_tree(lp_d, Q, parent, tokens=tok_d, token=token, stream=stream) == ok
+        rc, vis = dd.ddtv_build_visibility(parent, prefix, B, Q, vis_buf, stream=stream)
+        assert rc == ok
+        if "ws" not in state:
+            need = dd.ddtv_workspace_bytes(vis, H, w.kv_dtype)
+            state["ws"] = (torch.empty(max(need, 1), dtype=torch.uint8, device=dev), need)
+        ws, need = state["ws"]
+        assert dd.ddtv_append_kv(lat, k_pe, vis, r.ckv, r.k_rope, w.kv_dtype, nb.theta, stream=stream) == ok
+        assert dd.ddtv_prepare_query(q, w_kc, vis, q_abs, q_rope, nb.theta, stream=stream) == ok
+        assert dd.ddtv_verify_attn(q_abs, q_rope, r.ckv, r.k_rope, w.kv_dtype, H, vis, w.scale, r.out, r.lse, ws,
+                                   need, stream=stream) == ok
+        assert dd.ddtv_value_proj(r.out, w_vc, v, stream=stream) == ok
+        assert dd.ddtv_tree_accept(logits, parent, token, vis, pred, path, out_tok, alen, ckv=r.ckv,
+                                   k_rope=r.k_rope, kv_dtype=w.kv_dtype, stream=stream) == ok
+        state["vis"] = vis   # keep the struct's borrowed arrays alive until the stream drains
+    for _ in range(warmup):
+        iteration()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for _ in range(steps):
+        iteration()
+    hip.record(e1, stream)
+    us = hip.elapsed_ms(e0, e1) * 1e3 / steps
+    return {"workload": f"builder (top-{K} per depth, depth {D}) -> visibility -> cache append -> query prep "
+                        f"(d_nope 128) -> attention -> value projection (d_v 128) -> acceptance over {V} logits "
+                        "per node with compaction, on the benchmarked batch and cache",
+            "us_per_iteration": round(us, 2), "tree_tokens_per_s": round(B * Q / (us * 1e-6), 1),
+            "iterations": steps}
+
+
 def time_fp8_cache(dd, hip, stream, r, flops, steps=10, warmup=2):
     """The same verify call on an FP8 E4M3 copy of the benchmarked cache (a quarter
     of the fp32 bytes; widened exactly in the kernel): average call time from HIP
@@ -464,6 +521,7 @@ def main():
     out["tree_accept"] = time_tree_accept(dd, hip, stream, r)
     out["neighbour"] = time_neighbour(dd, hip, stream, r)
     out["fp8_cache"] = time_fp8_cache(dd, hip, stream, r, flops)
+    out["iteration"] = time_iteration(dd, hip, stream, r)
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(w, budget_s=args.cpu_budget)
