@@ -397,9 +397,11 @@ ddtv_status ddtv_value_proj(const float *latent, int64_t M, int32_t H, int32_t d
  * (the rows ddtv_verify_attn reads for the tree).  Other rows are untouched.
  *   latent  DEVICE float [B][Q][512] (16-byte aligned); k_pe DEVICE float [B][Q][64]
  *   vis, positions, rope_theta  as above
- *   ckv, k_rope  DEVICE caches ([total_kv][512], [total_kv][64]) of kv_dtype; bf16
- *           caches receive round-to-nearest-even values (finite inputs); ckv
- *           16-byte aligned
+ *   ckv, k_rope  DEVICE caches ([total_kv][512], [total_kv][64]) of kv_dtype; ckv
+ *           16-byte aligned.  Narrow caches receive the values rounded to nearest,
+ *           ties to even: bf16 from the float32 value; FP8 E4M3 likewise, with
+ *           magnitudes above 464 saturated to 448 (the largest finite code).
+ *           Inputs must be finite (NaN and infinities are not encoded).
  * Errors: DDTV_EINVAL (null or misaligned pointers, bad theta, bad vis),
  * DDTV_EUNSUPPORTED (dtype), DDTV_EDEVICE.
  */
