@@ -470,14 +470,16 @@ ddtv_status ddtv_verify_attn_tail(const float* q_abs, const float* q_rope, const
     if (st) return st;
     if (!workspace || workspace_bytes < L.total) return DDTV_EWORKSPACE;
     if (!aligned(workspace, 256)) return DDTV_EINVAL;
-    if (!opts || (opts->path == DDTV_PATH_AUTO && opts->split_len == 0)) {
+    // tree-sparse route (one workgroup of 512 threads per node and 16 heads; the
+    // grid's work-items must stay below 2^32)
+    const int64_t sparse_items = (int64_t)vis->B * vis->Q * ((H + 15) / 16) * 512;
+    if ((!opts || (opts->path == DDTV_PATH_AUTO && opts->split_len == 0)) && sparse_items <= (int64_t)UINT32_MAX) {
         // tree-sparse route: each node visits only its ancestors-or-self
         if (!q_abs || !q_rope || !ckv || !k_rope) return DDTV_EINVAL;
         if (!aligned(q_abs, 16) || !aligned(q_rope, 16) || !aligned(ckv, 16) || !aligned(k_rope, 16) ||
             !aligned(out, 16) || (lse && !aligned(lse, 4)))
             return DDTV_EINVAL;
         if (!std::isfinite(scale)) return DDTV_EINVAL;
-        if ((int64_t)vis->B * vis->Q > (int64_t)INT32_MAX) return DDTV_EUNSUPPORTED;
         TailSparseArgs a;
         a.q_abs = q_abs;
         a.q_rope = q_rope;

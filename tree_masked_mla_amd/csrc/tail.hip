@@ -62,10 +62,13 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(float* __restrict__ out
 }
 
 // ---- tree-sparse route ------------------------------------------------------
-// A wave takes 4 heads at a time; lane l holds latent dims 8l .. 8l+7 and rope
-// dim l of the query and of each visited cache row, so a cache row is read once
-// per wave for 4 heads and a score is a 9-term lane product plus a wave sum.
-constexpr int kSparseHeads = 4;
+// A workgroup of 8 waves takes one tree node and 16 of its heads, a wave 2 of
+// them; lane l holds latent dims 8l .. 8l+7 and rope dim l of the query and of
+// each visited cache row, so a cache row is read once per wave for 2 heads and a
+// score is a 9-term lane product plus a wave sum.  The next row's loads are in
+// flight while the current one is scored.
+constexpr int kSparseHeads = 2;
+constexpr int kSparseWaves = 8;
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -94,15 +97,20 @@ __device__ __forceinline__ void load_cache_row(const TailSparseArgs& a, int64_t 
 }
 
 template <int KV>
-__global__ __launch_bounds__(256) void tail_sparse_kernel(TailSparseArgs a) {
-    const int64_t node = blockIdx.x;
+__global__ __launch_bounds__(kSparseWaves * 64) void tail_sparse_kernel(TailSparseArgs a) {
+    // workgroup = (tree node, group of kSparseWaves * kSparseHeads heads)
+    const int n_hg = (a.H + kSparseWaves * kSparseHeads - 1) / (kSparseWaves * kSparseHeads);
+    const int64_t node = blockIdx.x / n_hg;
+    const int hg = (int)(blockIdx.x % n_hg);
     const int b = (int)(node / a.Q);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const ddtv_row rd = a.rows[b];
     const int64_t base = rd.kv_off + rd.prefix;          // cache row of tree node 0
     const uint32_t* mw = a.bits + node * a.W;
 
-    for (int h0 = wave * kSparseHeads; h0 < a.H; h0 += 4 * kSparseHeads) {
+    {
+        const int h0 = (hg * kSparseWaves + wave) * kSparseHeads;
+        if (h0 >= a.H) return;
         float qa[kSparseHeads][8], qr[kSparseHeads], m[kSparseHeads], l[kSparseHeads], acc[kSparseHeads][8];
 #pragma unroll
         for (int k = 0; k < kSparseHeads; ++k) {
@@ -120,28 +128,44 @@ __global__ __launch_bounds__(256) void tail_sparse_kernel(TailSparseArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
         }
-        for (int w = 0; w < a.W; ++w) {
-            uint32_t word = mw[w];
-            while (word) {
-                const int anc = 32 * w + __builtin_ctz(word);
-                word &= word - 1;
-                float v[8], r;
-                load_cache_row<KV>(a, base + anc, lane, v, r);
-#pragma unroll
-                for (int k = 0; k < kSparseHeads; ++k) {
-                    float s = qr[k] * r;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) s = fmaf(qa[k][e], v[e], s);
-                    s = wave_sum(s);                       // score in log2 units
-                    const float mn = fmaxf(m[k], s);
-                    const float alpha = exp2f(m[k] - mn);  // 0 on the first row (m = -inf)
-                    const float pr = exp2f(s - mn);
-                    l[k] = l[k] * alpha + pr;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[k][e] = fmaf(pr, v[e], acc[k][e] * alpha);
-                    m[k] = mn;
-                }
+        // the ancestors-or-self in index order (set bits of the mask), the next
+        // row's loads in flight while the current one is scored
+        int w = 0;
+        uint32_t word = mw[0];
+        auto next_anc = [&]() -> int {   // -1 once the mask is exhausted
+            while (word == 0u) {
+                if (++w >= a.W) return -1;
+                word = mw[w];
             }
+            const int anc = 32 * w + __builtin_ctz(word);
+            word &= word - 1;
+            return anc;
+        };
+        int cur = next_anc();
+        float v[8], r = 0.f;
+        if (cur >= 0) load_cache_row<KV>(a, base + cur, lane, v, r);
+        while (cur >= 0) {
+            const int nxt = next_anc();
+            float vn[8], rn = 0.f;
+            if (nxt >= 0) load_cache_row<KV>(a, base + nxt, lane, vn, rn);
+#pragma unroll
+            for (int k = 0; k < kSparseHeads; ++k) {
+                float s = qr[k] * r;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s = fmaf(qa[k][e], v[e], s);
+                s = wave_sum(s);                       // score in log2 units
+                const float mn = fmaxf(m[k], s);
+                const float alpha = exp2f(m[k] - mn);  // 0 on the first row (m = -inf)
+                const float pr = exp2f(s - mn);
+                l[k] = l[k] * alpha + pr;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[k][e] = fmaf(pr, v[e], acc[k][e] * alpha);
+                m[k] = mn;
+            }
+            cur = nxt;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = vn[e];
+            r = rn;
         }
         // merge with the prefix result: weights e^(lse - M) of both sides
 #pragma unroll
@@ -198,13 +222,14 @@ namespace ddtv {
 
 hipError_t launch_tail_sparse(const TailSparseArgs& a, int kv_dtype, hipStream_t stream) {
     (void)hipGetLastError();
-    const dim3 grid((unsigned)((int64_t)a.B * a.Q));
+    const int n_hg = (a.H + kSparseWaves * kSparseHeads - 1) / (kSparseWaves * kSparseHeads);
+    const dim3 grid((unsigned)((int64_t)a.B * a.Q * n_hg));
     if (kv_dtype == DDTV_BF16)
-        hipLaunchKernelGGL(tail_sparse_kernel<DDTV_BF16>, grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(tail_sparse_kernel<DDTV_BF16>, grid, dim3(kSparseWaves * 64), 0, stream, a);
     else if (kv_dtype == DDTV_FP8_E4M3)
-        hipLaunchKernelGGL(tail_sparse_kernel<DDTV_FP8_E4M3>, grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(tail_sparse_kernel<DDTV_FP8_E4M3>, grid, dim3(kSparseWaves * 64), 0, stream, a);
     else
-        hipLaunchKernelGGL(tail_sparse_kernel<DDTV_F32>, grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(tail_sparse_kernel<DDTV_F32>, grid, dim3(kSparseWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
