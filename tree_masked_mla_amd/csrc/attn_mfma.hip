@@ -356,16 +356,20 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
     // pre-multiplied by scale*log2(e) so the scores come out in exp2 units.
     const int myrow = rt * kRows + pair * 16 + n;
     const bool row_ok = myrow < a.R;
+    // The 18 loads are unconditional (a row past the end reads row 0 and scales it
+    // by 0), so they issue back to back under one wait; a per-load row test made
+    // the compiler branch around each load and wait for it in turn.
     f32x4 qreg[18];
     {
         const int64_t qrow = (int64_t)b * a.R + (row_ok ? myrow : 0);
         const f32x4* qa = reinterpret_cast<const f32x4*>(a.q_abs) + qrow * 128;
         const f32x4* qr = reinterpret_cast<const f32x4*>(a.q_rope) + qrow * 16;
+        const float sc = row_ok ? a.scale_log2 : 0.f;
 #pragma unroll
         for (int t = 0; t < 18; ++t) {
             const int tg = 18 * HALF + t;
             const f32x4 v = (tg < 32) ? qa[4 * tg + g] : qr[4 * (tg - 32) + g];
-            qreg[t] = row_ok ? v * a.scale_log2 : f32x4{0.f, 0.f, 0.f, 0.f};
+            qreg[t] = v * sc;
         }
     }
     // mask words of this row's node (read only in the tiles that reach the tree)
