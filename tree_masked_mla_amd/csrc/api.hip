@@ -672,7 +672,7 @@ ddtv_status ddtv_prepare_query(const float* q, int32_t d_nope, int32_t H, const 
     p.Q = vis->Q;
     p.W = vis->W;
     rope_frequencies(rope_theta, p.inv_freq);
-    return launch_proj(p, false, stream) == hipSuccess ? DDTV_OK : DDTV_EDEVICE;
+    return launch_proj(p, false, cu_count(), stream) == hipSuccess ? DDTV_OK : DDTV_EDEVICE;
 }
 
 ddtv_status ddtv_value_proj(const float* latent, int64_t M, int32_t H, int32_t d_v, const float* w_vc, float* v,
@@ -696,7 +696,7 @@ ddtv_status ddtv_value_proj(const float* latent, int64_t M, int32_t H, int32_t d
     p.C = v;
     p.c_head = d_v;
     p.ldc = (int64_t)H * d_v;
-    return launch_proj(p, true, stream) == hipSuccess ? DDTV_OK : DDTV_EDEVICE;
+    return launch_proj(p, true, cu_count(), stream) == hipSuccess ? DDTV_OK : DDTV_EDEVICE;
 }
 
 ddtv_status ddtv_append_kv(const float* latent, const float* k_pe, const ddtv_vis* vis, const int32_t* positions,

@@ -21,13 +21,15 @@
 // stages of 32, double-buffered through LDS: 16-byte global loads, the next
 // stage loaded into registers while the current one feeds the MFMAs.  Each wave
 // owns 32 x 32 of the tile (2 x 2 blocks of 16 x 16); two workgroups fit a CU,
-// so every SIMD holds up to four waves to cover LDS reads and barriers.
+// so every SIMD holds up to four waves to cover LDS reads and barriers.  Small
+// grids (fewer wide workgroups than CUs) take 2-wave workgroups over 64 x 32
+// tiles instead, so the work spreads over four times as many CUs.
 // LDS layouts (4-byte words; 64 banks on gfx950):
 //   A stage   [64 m][36]   : lane (i, kk) of an A operand reads m = i, k = kk;
 //                            row stride 36 words puts the 16 x 4 lanes on 64
 //                            distinct banks;
-//   B stage   absorb: [32 k][144] (n contiguous; stride 144 = 16 mod 64 puts the
-//                            four k rows of an operand on disjoint bank groups)
+//   B stage   absorb: [32 k][BN + 16] (n contiguous; a stride of 16 mod 64 puts
+//                            the four k rows of an operand on disjoint bank groups)
 //             value:  [128 n][36] (k contiguous, as A).
 #include <math.h>
 
@@ -37,43 +39,56 @@
 namespace ddtv {
 namespace {
 
-constexpr int kBM = 64, kBN = 128, kBK = 32;
-constexpr int kThreadsProj = 512;
+constexpr int kBM = 64, kBK = 32;
 constexpr int kAStride = 36;             // words per m row of an A stage
-constexpr int kBStrideKN = 144;          // words per k row of a [k][n] B stage
 constexpr int kBStrideNK = 36;           // words per n row of an [n][k] B stage
-constexpr int kAStage = kBM * kAStride;                  // 2304 words
-constexpr int kBStage = kBK * kBStrideKN;                // 4608 words (= kBN * kBStrideNK)
-static_assert(kBK * kBStrideKN == kBN * kBStrideNK, "both B layouts fill the same stage");
+constexpr int kAStage = kBM * kAStride;  // 2304 words
+
+// Workgroup shape.  Wide: 8 waves over a 64 x 128 output tile (2 x 4 waves of
+// 32 x 32).  Narrow: 2 waves over 64 x 32, four times the workgroups, for grids
+// that would leave most CUs idle with wide tiles (few tree nodes and heads).
+template <bool kWide>
+struct Geo {
+    static constexpr int Threads = kWide ? 512 : 128;
+    static constexpr int BN = kWide ? 128 : 32;
+    static constexpr int WavesN = BN / 32;              // waves across the columns
+    static constexpr int BStrideKN = BN + 16;           // words per k row of a [k][n] B stage (16 mod 64)
+    static constexpr int BStage = (kBK * BStrideKN > BN * kBStrideNK) ? kBK * BStrideKN : BN * kBStrideNK;
+    static constexpr int ALoads = kBM * kBK / 4 / Threads;   // float4 per thread
+    static constexpr int BLoads = BN * kBK / 4 / Threads;
+    static constexpr int RopeRows = Threads / 16;
+    static_assert(kDLat / BN * RopeRows >= kBM, "the rotary slice covers a row tile with its column-tile workgroups");
+};
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
-// Global -> registers for one K stage.  A: 64 rows x 32 k = 512 float4, one per
-// thread (8 threads per row, 128 contiguous bytes).  B: 1024 float4, two per
-// thread: [k][n] rows of 512 bytes, or [n][k] rows of 128 bytes.
-template <bool kBTrans>
+// Global -> registers for one K stage.  A: 64 rows x 32 k = 512 float4 (8 threads
+// per row, 128 contiguous bytes).  B: 32 k x BN n, as [k][n] rows of 4 BN bytes
+// (absorb) or [n][k] rows of 128 bytes (value).
+template <bool kWide>
 struct Stage {
-    float4 a[1];
-    float4 b[2];
+    float4 a[Geo<kWide>::ALoads];
+    float4 b[Geo<kWide>::BLoads];
 };
 
-template <bool kBTrans>
-__device__ __forceinline__ void load_stage(const ProjArgs& p, int h, int m0, int n0, int k0, Stage<kBTrans>& s) {
+template <bool kBTrans, bool kWide>
+__device__ __forceinline__ void load_stage(const ProjArgs& p, int h, int m0, int n0, int k0, Stage<kWide>& s) {
+    using G = Geo<kWide>;
     const int t = threadIdx.x;
 #pragma unroll
-    for (int r = 0; r < 1; ++r) {
-        const int idx = t + r * kThreadsProj;
+    for (int r = 0; r < G::ALoads; ++r) {
+        const int idx = t + r * G::Threads;
         const int row = idx >> 3, kq = (idx & 7) * 4;
         const int64_t m = (int64_t)m0 + row;
         s.a[r] = m < p.M ? ld4(p.A + m * p.lda + (int64_t)h * p.a_head + k0 + kq) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int idx = t + r * kThreadsProj;
+    for (int r = 0; r < G::BLoads; ++r) {
+        const int idx = t + r * G::Threads;
         if (!kBTrans) {
-            const int k = idx >> 5, nq = (idx & 31) * 4;       // 32 float4 per k row
+            const int k = idx / (G::BN / 4), nq = (idx % (G::BN / 4)) * 4;
             const int n = n0 + nq;
             s.b[r] = n < p.N ? ld4(p.B + (int64_t)h * p.b_head + (int64_t)(k0 + k) * p.N + n)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -86,21 +101,22 @@ __device__ __forceinline__ void load_stage(const ProjArgs& p, int h, int m0, int
     }
 }
 
-template <bool kBTrans>
-__device__ __forceinline__ void store_stage(float* As, float* Bs, const Stage<kBTrans>& s) {
+template <bool kBTrans, bool kWide>
+__device__ __forceinline__ void store_stage(float* As, float* Bs, const Stage<kWide>& s) {
+    using G = Geo<kWide>;
     const int t = threadIdx.x;
 #pragma unroll
-    for (int r = 0; r < 1; ++r) {
-        const int idx = t + r * kThreadsProj;
+    for (int r = 0; r < G::ALoads; ++r) {
+        const int idx = t + r * G::Threads;
         const int row = idx >> 3, kq = (idx & 7) * 4;
         *reinterpret_cast<float4*>(As + row * kAStride + kq) = s.a[r];
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int idx = t + r * kThreadsProj;
+    for (int r = 0; r < G::BLoads; ++r) {
+        const int idx = t + r * G::Threads;
         if (!kBTrans) {
-            const int k = idx >> 5, nq = (idx & 31) * 4;
-            *reinterpret_cast<float4*>(Bs + k * kBStrideKN + nq) = s.b[r];
+            const int k = idx / (G::BN / 4), nq = (idx % (G::BN / 4)) * 4;
+            *reinterpret_cast<float4*>(Bs + k * G::BStrideKN + nq) = s.b[r];
         } else {
             const int nl = idx >> 3, kq = (idx & 7) * 4;
             *reinterpret_cast<float4*>(Bs + nl * kBStrideNK + kq) = s.b[r];
@@ -108,13 +124,10 @@ __device__ __forceinline__ void store_stage(float* As, float* Bs, const Stage<kB
     }
 }
 
-// NeoX rotation of the rope part of 32 query rows (m0 .. m0+31), every head.
+// NeoX rotation of the rope part of kThreads / 16 query rows from m0, every head.
 // 16 lanes per row, two pairs per lane: each (row, pair) angle is computed once
 // and used for all heads.  Angles, their sine and cosine, and the rotation run
 // in float64; the result is rounded once to float32.
-constexpr int kRopeRows = kThreadsProj / 16;
-static_assert(kDLat / kBN * kRopeRows >= kBM, "the rotary slice covers a row tile with its column-tile workgroups");
-
 __device__ void rope_rows(const ProjArgs& p, int64_t m0) {
     const int64_t m = m0 + (threadIdx.x >> 4);
     const int i = (threadIdx.x & 15) * 2;
@@ -148,23 +161,25 @@ __device__ void rope_rows(const ProjArgs& p, int64_t m0) {
     }
 }
 
-template <bool kBTrans>
-__global__ __launch_bounds__(kThreadsProj) void proj_gemm_kernel(ProjArgs p) {
+template <bool kBTrans, bool kWide>
+__global__ __launch_bounds__(Geo<kWide>::Threads) void proj_gemm_kernel(ProjArgs p) {
+    using G = Geo<kWide>;
     __shared__ float As[2][kAStage];
-    __shared__ float Bs[2][kBStage];
+    __shared__ float Bs[2][G::BStage];
     // With the rotary step, slice z = 0 rotates (dispatched first, short) and
     // slice z = 1 + h multiplies head h.
     int h = blockIdx.z;
     if (!kBTrans && p.rope_out) {
         if (h == 0) {
-            if (blockIdx.y * kRopeRows < kBM) rope_rows(p, (int64_t)blockIdx.x * kBM + blockIdx.y * kRopeRows);
+            if (blockIdx.y * G::RopeRows < kBM)
+                rope_rows(p, (int64_t)blockIdx.x * kBM + blockIdx.y * G::RopeRows);
             return;
         }
         --h;
     }
-    const int m0 = blockIdx.x * kBM, n0 = blockIdx.y * kBN;
+    const int m0 = blockIdx.x * kBM, n0 = blockIdx.y * G::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = (wave >> 2) * 32, wn = (wave & 3) * 32;
+    const int wm = (wave / G::WavesN) * 32, wn = (wave % G::WavesN) * 32;
     const int li = lane & 15, lk = lane >> 4;
 
     floatx4 acc[2][2];
@@ -173,14 +188,14 @@ __global__ __launch_bounds__(kThreadsProj) void proj_gemm_kernel(ProjArgs p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    Stage<kBTrans> st;
-    load_stage<kBTrans>(p, h, m0, n0, 0, st);
-    store_stage<kBTrans>(As[0], Bs[0], st);
+    Stage<kWide> st;
+    load_stage<kBTrans, kWide>(p, h, m0, n0, 0, st);
+    store_stage<kBTrans, kWide>(As[0], Bs[0], st);
     __syncthreads();
     const int n_stage = p.K / kBK;
     for (int s = 0; s < n_stage; ++s) {
         const int cur = s & 1;
-        if (s + 1 < n_stage) load_stage<kBTrans>(p, h, m0, n0, (s + 1) * kBK, st);
+        if (s + 1 < n_stage) load_stage<kBTrans, kWide>(p, h, m0, n0, (s + 1) * kBK, st);
         const float* A = As[cur];
         const float* Bm = Bs[cur];
 #pragma unroll
@@ -191,7 +206,7 @@ __global__ __launch_bounds__(kThreadsProj) void proj_gemm_kernel(ProjArgs p) {
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 b[j] = kBTrans ? Bm[(wn + j * 16 + li) * kBStrideNK + kk + lk]
-                               : Bm[(kk + lk) * kBStrideKN + wn + j * 16 + li];
+                               : Bm[(kk + lk) * G::BStrideKN + wn + j * 16 + li];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -199,7 +214,7 @@ __global__ __launch_bounds__(kThreadsProj) void proj_gemm_kernel(ProjArgs p) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
         }
         if (s + 1 < n_stage) {
-            store_stage<kBTrans>(As[cur ^ 1], Bs[cur ^ 1], st);
+            store_stage<kBTrans, kWide>(As[cur ^ 1], Bs[cur ^ 1], st);
             __syncthreads();
         }
     }
@@ -307,13 +322,22 @@ __global__ __launch_bounds__(64) void append_kv_kernel(AppendArgs p) {
 }  // namespace
 
 
-hipError_t launch_proj(const ProjArgs& p, bool b_trans, hipStream_t stream) {
-    const dim3 grid((unsigned)((p.M + kBM - 1) / kBM), (unsigned)((p.N + kBN - 1) / kBN),
-                    (unsigned)(p.H + (!b_trans && p.rope_out ? 1 : 0)));
+template <bool kBTrans, bool kWide>
+static void launch_proj_as(const ProjArgs& p, hipStream_t stream) {
+    using G = Geo<kWide>;
+    const dim3 grid((unsigned)((p.M + kBM - 1) / kBM), (unsigned)((p.N + G::BN - 1) / G::BN),
+                    (unsigned)(p.H + (!kBTrans && p.rope_out ? 1 : 0)));
+    hipLaunchKernelGGL((proj_gemm_kernel<kBTrans, kWide>), grid, dim3(G::Threads), 0, stream, p);
+}
+
+hipError_t launch_proj(const ProjArgs& p, bool b_trans, int cus, hipStream_t stream) {
+    // narrow tiles when wide ones would give fewer workgroups than CUs
+    const int64_t wide_wgs = (p.M + kBM - 1) / kBM * ((p.N + Geo<true>::BN - 1) / Geo<true>::BN) * p.H;
+    const bool wide = wide_wgs >= cus;
     if (b_trans)
-        hipLaunchKernelGGL(proj_gemm_kernel<true>, grid, dim3(kThreadsProj), 0, stream, p);
+        wide ? launch_proj_as<true, true>(p, stream) : launch_proj_as<true, false>(p, stream);
     else
-        hipLaunchKernelGGL(proj_gemm_kernel<false>, grid, dim3(kThreadsProj), 0, stream, p);
+        wide ? launch_proj_as<false, true>(p, stream) : launch_proj_as<false, false>(p, stream);
     return hipGetLastError();
 }
 

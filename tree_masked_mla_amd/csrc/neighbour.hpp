@@ -41,7 +41,8 @@ struct AppendArgs {
     double inv_freq[32];
 };
 
-hipError_t launch_proj(const ProjArgs& p, bool b_trans, hipStream_t stream);
+// cus: compute units of the device (small grids take narrower tiles)
+hipError_t launch_proj(const ProjArgs& p, bool b_trans, int cus, hipStream_t stream);
 hipError_t launch_append_kv(const AppendArgs& p, hipStream_t stream);
 
 }  // namespace ddtv
