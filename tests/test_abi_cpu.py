@@ -339,3 +339,40 @@ def test_plan_cache_is_thread_safe(lib):
         for _ in range(3):
             got = list(ex.map(plan, shapes * 4))
             assert got == [expected[s] for s in shapes * 4]
+
+
+def test_header_is_c11_and_links_from_c(lib, tmp_path):
+    """include/ddtv.h compiles as C11 (gcc, warnings as errors) and a C program links
+    against libddtv.so and calls it: the version, a status string and an argument
+    error reported before any HIP call (no GPU needed)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "use_ddtv.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <string.h>
+#include "ddtv.h"
+int main(void) {
+    ddtv_vis vis;
+    memset(&vis, 0, sizeof vis);
+    if (ddtv_version() <= 0) return 1;
+    if (strcmp(ddtv_status_string(DDTV_EINVAL), "invalid argument") != 0) return 2;
+    /* null inputs and an empty visibility: rejected on the host */
+    if (ddtv_verify_attn(NULL, NULL, NULL, NULL, DDTV_F32, 8, &vis, 0.07f, NULL, NULL, NULL, 0, NULL) != DDTV_EINVAL)
+        return 3;
+    if (ddtv_vis_bytes(0, 9) != 0 || ddtv_vis_bytes(1, 9) == 0) return 4;
+    printf("%d\n", (int)ddtv_version());
+    return 0;
+}
+''')
+    exe = tmp_path / "use_ddtv"
+    libdir = os.path.dirname(dd.LIB_PATH)
+    cmd = ["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           "-I" + os.path.join(ROOT, "include"), str(src), "-L" + libdir, "-lddtv", "-Wl,-rpath," + libdir,
+           "-o", str(exe)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    assert int(r.stdout.strip()) == dd.ddtv_version()
