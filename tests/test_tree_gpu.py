@@ -49,6 +49,8 @@ def assert_same_tree(got, ref, what):
     (1, 4, 64, 200),      # most choices per depth
     (70, 8, 3, 40),       # many batch rows
     (2, 3, 2, 15),        # exactly the full tree of depth 3
+    (2, 8, 4, 65),        # just past the smallest register-slot instantiation (Q <= 64)
+    (2, 8, 4, 129),       # just past the middle one (Q <= 128)
 ])
 def test_tree_matches_oracle(B, D, K, Q):
     say(f"tree B{B} D{D} K{K} Q{Q}")

@@ -40,9 +40,12 @@ namespace ddtv {
 
 namespace {
 
-constexpr int kSlots = 5;                 // 64 lanes x 5 >= kMaxQ + 1 candidates
-constexpr int kNodeSlots = kMaxQ / 64;    // 64 lanes x 4 = kMaxQ taken nodes
-static_assert(64 * kSlots >= kMaxQ + 1, "candidate slots");
+// Register slots per lane: kSlots candidate slots (64 * kSlots >= Q + 1 candidates)
+// and kNodeSlots taken-node slots (64 * kNodeSlots >= Q), instantiated per tree
+// size so small trees scan fewer slots per step: (2, 1) for Q <= 64, (3, 2) for
+// Q <= 128, (5, 4) up to kMaxQ.
+constexpr int kMaxSlots = 5;              // 64 lanes x 5 >= kMaxQ + 1 candidates
+static_assert(64 * kMaxSlots >= kMaxQ + 1, "candidate slots");
 
 // float -> unsigned with the same order (-0 and +0 map to the same value)
 __device__ __forceinline__ uint32_t score_key(float s) {
@@ -71,6 +74,7 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
     return max(max(r0, r1), max(r2, r3));
 }
 
+template <int kSlots, int kNodeSlots>
 __global__ __launch_bounds__(64) void tree_build_kernel(TreeArgs a) {
     extern __shared__ float slp[];       // [Ds][Ks] staged log-probabilities
     __shared__ uint32_t ncode[kMaxQ];    // taken node i: (parent + 1) << 16 | (rank + 1) << 8 | depth
@@ -189,8 +193,14 @@ size_t tree_build_lds_bytes(int D, int K, int Q) { return sizeof(float) * (size_
 
 hipError_t launch_tree_build(const TreeArgs& a, hipStream_t stream) {
     (void)hipGetLastError();   // report only this launch's error
-    hipLaunchKernelGGL(tree_build_kernel, dim3((unsigned)a.B), dim3(64), tree_build_lds_bytes(a.D, a.K, a.Q), stream,
-                       a);
+    const size_t lds = tree_build_lds_bytes(a.D, a.K, a.Q);
+    if (a.Q <= 64)
+        hipLaunchKernelGGL((tree_build_kernel<2, 1>), dim3((unsigned)a.B), dim3(64), lds, stream, a);
+    else if (a.Q <= 128)
+        hipLaunchKernelGGL((tree_build_kernel<3, 2>), dim3((unsigned)a.B), dim3(64), lds, stream, a);
+    else
+        hipLaunchKernelGGL((tree_build_kernel<kMaxSlots, kMaxQ / 64>), dim3((unsigned)a.B), dim3(64), lds, stream,
+                           a);
     return hipGetLastError();
 }
 
