@@ -66,7 +66,10 @@ __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast
 
 // Global -> registers for one K stage.  A: 64 rows x 32 k = 512 float4 (8 threads
 // per row, 128 contiguous bytes).  B: 32 k x BN n, as [k][n] rows of 4 BN bytes
-// (absorb) or [n][k] rows of 128 bytes (value).
+// (absorb) or [n][k] rows of 128 bytes (value).  Rows past M and columns past N
+// read the last valid row or column instead of a zero fill: they feed only
+// outputs that are never stored, and unconditional loads let the compiler keep
+// them in flight across the stage instead of waiting at each predicated load.
 template <bool kWide>
 struct Stage {
     float4 a[Geo<kWide>::ALoads];
@@ -81,22 +84,20 @@ __device__ __forceinline__ void load_stage(const ProjArgs& p, int h, int m0, int
     for (int r = 0; r < G::ALoads; ++r) {
         const int idx = t + r * G::Threads;
         const int row = idx >> 3, kq = (idx & 7) * 4;
-        const int64_t m = (int64_t)m0 + row;
-        s.a[r] = m < p.M ? ld4(p.A + m * p.lda + (int64_t)h * p.a_head + k0 + kq) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int64_t m = min((int64_t)m0 + row, p.M - 1);
+        s.a[r] = ld4(p.A + m * p.lda + (int64_t)h * p.a_head + k0 + kq);
     }
 #pragma unroll
     for (int r = 0; r < G::BLoads; ++r) {
         const int idx = t + r * G::Threads;
         if (!kBTrans) {
             const int k = idx / (G::BN / 4), nq = (idx % (G::BN / 4)) * 4;
-            const int n = n0 + nq;
-            s.b[r] = n < p.N ? ld4(p.B + (int64_t)h * p.b_head + (int64_t)(k0 + k) * p.N + n)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
+            const int n = min(n0 + nq, p.N - 4);           // N is a multiple of 4 here (512)
+            s.b[r] = ld4(p.B + (int64_t)h * p.b_head + (int64_t)(k0 + k) * p.N + n);
         } else {
             const int nl = idx >> 3, kq = (idx & 7) * 4;       // 8 float4 per n row
-            const int n = n0 + nl;
-            s.b[r] = n < p.N ? ld4(p.B + (int64_t)h * p.b_head + (int64_t)n * p.K + k0 + kq)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
+            const int n = min(n0 + nl, p.N - 1);
+            s.b[r] = ld4(p.B + (int64_t)h * p.b_head + (int64_t)n * p.K + k0 + kq);
         }
     }
 }
