@@ -134,7 +134,7 @@ size_t ddtv_vis_bytes(int32_t B, int32_t Q);
  * Nodes come out in the order they were taken, so scores are non-increasing when
  * the input is sorted.  Errors: DDTV_EINVAL (null logp or parent, misaligned
  * pointers, B < 1, D < 1, Q outside 1..DDTV_MAX_Q, Q beyond the depth-D tree),
- * DDTV_EUNSUPPORTED (K outside 1..64), DDTV_EDEVICE.
+ * DDTV_EUNSUPPORTED (K outside 1..64, B above 2^26), DDTV_EDEVICE.
  */
 ddtv_status ddtv_build_tree(const float *logp, const int32_t *tokens, int32_t B, int32_t D, int32_t K,
                             int32_t Q, int32_t *parent, int32_t *depth, int32_t *rank, int32_t *token,
@@ -330,7 +330,7 @@ ddtv_status ddtv_plan_info(const ddtv_vis *vis, int32_t H, ddtv_dtype kv_dtype,
  *   kv_dtype    their element type
  *   pred, path, out_tokens  DEVICE int32 [B][Q] out;  accept_len DEVICE int32 [B] out
  * Errors: DDTV_EINVAL (null or misaligned pointers, V < 1, one cache without the
- * other, a bad vis), DDTV_EUNSUPPORTED (dtype), DDTV_EDEVICE.
+ * other, a bad vis), DDTV_EUNSUPPORTED (dtype, more than 2^24 nodes), DDTV_EDEVICE.
  */
 ddtv_status ddtv_tree_accept(const float *logits, int32_t V, const int32_t *parent,
                              const int32_t *token, const ddtv_vis *vis, void *ckv, void *k_rope,
@@ -373,7 +373,7 @@ ddtv_status ddtv_tree_accept(const float *logits, int32_t V, const int32_t *pare
  *   q_rope  DEVICE float [B][Q][H][64] out: the rope part, rotated
  * The outputs are exactly the q_abs / q_rope operands of ddtv_verify_attn.
  * Errors: DDTV_EINVAL (null or misaligned pointers, H outside 1..1024, bad theta,
- * bad vis), DDTV_EUNSUPPORTED (d_nope, more than 2^30 nodes), DDTV_EDEVICE.
+ * bad vis), DDTV_EUNSUPPORTED (d_nope, more than 2^28 nodes), DDTV_EDEVICE.
  */
 ddtv_status ddtv_prepare_query(const float *q, int32_t d_nope, int32_t H, const ddtv_vis *vis,
                                const int32_t *positions, double rope_theta, const float *w_kc,
@@ -386,7 +386,7 @@ ddtv_status ddtv_prepare_query(const float *q, int32_t d_nope, int32_t H, const 
  *   v       DEVICE float [M][H][d_v] out: v[m][h][n] = sum_c latent[m][h][c] w_vc[h][n][c]
  *   d_v     1..512
  * M = 0 is a no-op.  Errors: DDTV_EINVAL (null or misaligned pointers, M < 0,
- * H outside 1..1024), DDTV_EUNSUPPORTED (d_v, M above 2^30), DDTV_EDEVICE.
+ * H outside 1..1024), DDTV_EUNSUPPORTED (d_v, M above 2^28), DDTV_EDEVICE.
  */
 ddtv_status ddtv_value_proj(const float *latent, int64_t M, int32_t H, int32_t d_v, const float *w_vc,
                             float *v, hipStream_t stream);
@@ -403,7 +403,7 @@ ddtv_status ddtv_value_proj(const float *latent, int64_t M, int32_t H, int32_t d
  *           magnitudes above 464 saturated to 448 (the largest finite code).
  *           Inputs must be finite (NaN and infinities are not encoded).
  * Errors: DDTV_EINVAL (null or misaligned pointers, bad theta, bad vis),
- * DDTV_EUNSUPPORTED (dtype), DDTV_EDEVICE.
+ * DDTV_EUNSUPPORTED (dtype, more than 2^26 nodes), DDTV_EDEVICE.
  */
 ddtv_status ddtv_append_kv(const float *latent, const float *k_pe, const ddtv_vis *vis,
                            const int32_t *positions, double rope_theta, void *ckv, void *k_rope,

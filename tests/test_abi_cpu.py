@@ -154,6 +154,7 @@ def test_build_tree_argument_checks(lib):
     assert call(Q=257) == E
     assert call(K=0) == U
     assert call(K=65) == U
+    assert call(B=(1 << 26) + 1) == U                 # B x 64 work-items past 2^32
     assert call(D=2, K=2, Q=8) == E                   # the depth-2 binary tree has 7 nodes
     assert call(D=1, K=64, Q=66) == E
 
@@ -175,6 +176,8 @@ def test_tree_accept_argument_checks(lib):
     assert call(ckv=FAKE) == E                        # one cache without the other
     assert call(ckv=FAKE + 8, k_rope=FAKE) == E       # misaligned cache
     assert call(ckv=FAKE, k_rope=FAKE, dtype=5) == U
+    big = fake_vis(B=(1 << 18) + 1, Q=64, prefix=np.zeros((1 << 18) + 1, np.int32))
+    assert call(v=big) == U                           # B x Q x 256 work-items past 2^32
 
 
 def test_tail_mode_argument_checks(lib):
@@ -226,7 +229,7 @@ def test_neighbour_argument_checks(lib):
     assert vproj(H=0) == E
     assert vproj(d_v=0) == U
     assert vproj(d_v=513) == U
-    assert vproj(M=(1 << 30) + 1) == U
+    assert vproj(M=(1 << 28) + 1) == U
     assert vproj(M=0) == dd.DDTV_OK                 # nothing to do, nothing launched
 
     def app(lat=FAKE, kpe=FAKE, v=vis, pos=None, theta=50000.0, ckv=FAKE, kr=FAKE, dtype=0):
@@ -239,6 +242,8 @@ def test_neighbour_argument_checks(lib):
     assert app(v=None) == E
     assert app(theta=0.0) == E
     assert app(dtype=7) == U
+    big = fake_vis(B=(1 << 20) + 1, Q=64, prefix=np.zeros((1 << 20) + 1, np.int32))
+    assert app(v=big) == U                            # B x Q x 64 work-items past 2^32
 
 
 def test_plan_rules(lib):
@@ -251,6 +256,9 @@ def test_plan_rules(lib):
         assert rc == 0 and path == want, (Q, H, path)
     vis = fake_vis(B=1, Q=9, prefix=(100,))
     assert dd.ddtv_plan_info(vis, 8, 0, dd.make_opts(path=dd.DDTV_PATH_MFMA))[1] == dd.DDTV_PATH_MFMA
+    # a grid past 2^32 work-items is refused before any launch
+    big = fake_vis(B=(1 << 16) + 1, Q=256, prefix=np.zeros((1 << 16) + 1, np.int32))
+    assert dd.ddtv_plan_info(big, 128, 0)[0] == dd.DDTV_EUNSUPPORTED
     # a forced split length gives ceil(max_kv / L) splits and a matching workspace
     vis = fake_vis(B=2, Q=64, prefix=(1000, 5000))
     opts = dd.make_opts(split_len=1024)

@@ -64,8 +64,15 @@ int cu_count() {
     return cached[dev];
 }
 
+// A dispatch packet holds each grid dimension's work-item count in 32 bits, so
+// `workgroups` workgroups of `threads` threads along one dimension must stay
+// below 2^32.
+bool grid_fits(int64_t workgroups, int threads) {
+    return workgroups >= 0 && workgroups <= (int64_t)UINT32_MAX / threads;
+}
+
 constexpr int32_t kMaxProjHeads = 1024;          // heads per projection call (grid z)
-constexpr int64_t kMaxProjRows = (int64_t)1 << 30; // tokens per projection call (grid x * 256 threads < 2^32)
+constexpr int64_t kMaxProjRows = (int64_t)1 << 28; // tokens per projection call: (rows / 64) x 512 threads < 2^32
 
 bool dtype_ok(int d) { return d == DDTV_F32 || d == DDTV_BF16 || d == DDTV_FP8_E4M3; }
 
@@ -305,7 +312,8 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     }
     p->n_split = (max_kv + p->split_len - 1) / p->split_len;
     p->grid = (int64_t)vis->B * p->n_rt * p->n_split;
-    if (p->grid > (int64_t)UINT32_MAX) return DDTV_EUNSUPPORTED;
+    if (!grid_fits(p->grid, 512)) return DDTV_EUNSUPPORTED;   // 512 = the largest attention workgroup
+    if (p->n_split > 1 && !grid_fits(((int64_t)vis->B * R + 1) / 2, 256)) return DDTV_EUNSUPPORTED;   // merge
     if (p->n_split > 1) {
         const size_t rows_total = (size_t)vis->B * p->n_split * (size_t)R;
         p->ws_part_o = 0;
@@ -343,6 +351,7 @@ ddtv_status tail_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const
     const ddtv_vis t = tail_view(vis, vis->rows);   // geometry only: planning reads no device data
     st = make_plan(&t, H, kv_dtype, opts, p);
     if (st) return st;
+    if (!grid_fits(((int64_t)vis->B * vis->Q * H + 1) / 2, 256)) return DDTV_EUNSUPPORTED;   // tail merge
     L->rows = 0;
     L->lse = round_up((size_t)vis->B * sizeof(ddtv_row), 256);
     L->plan = L->lse + round_up((size_t)vis->B * vis->Q * (size_t)H * sizeof(float), 256);
@@ -430,6 +439,7 @@ ddtv_status ddtv_build_tree(const float* logp, const int32_t* tokens, int32_t B,
         return DDTV_EINVAL;
     if (B < 1 || D < 1 || Q < 1 || Q > kMaxQ) return DDTV_EINVAL;
     if (K < 1 || K > kMaxTreeK) return DDTV_EUNSUPPORTED;
+    if (!grid_fits(B, 64)) return DDTV_EUNSUPPORTED;
     // nodes of the full K-ary tree of depth D, counted until they reach Q
     int64_t nodes = 1, level = 1;
     for (int d = 1; d <= D && nodes < Q; ++d) {
@@ -529,7 +539,7 @@ ddtv_status ddtv_tree_accept(const float* logits, int32_t V, const int32_t* pare
         if (!aligned(ckv, 16) || !aligned(k_rope, 16)) return DDTV_EINVAL;
         if (!dtype_ok(kv_dtype)) return DDTV_EUNSUPPORTED;
     }
-    if ((int64_t)vis->B * vis->Q > (int64_t)UINT32_MAX) return DDTV_EUNSUPPORTED;
+    if (!grid_fits((int64_t)vis->B * vis->Q, 256)) return DDTV_EUNSUPPORTED;
     AcceptArgs a;
     a.logits = logits;
     a.parent = parent;
@@ -709,7 +719,7 @@ ddtv_status ddtv_append_kv(const float* latent, const float* k_pe, const ddtv_vi
     if (st) return st;
     if (!rope_ok(rope_theta)) return DDTV_EINVAL;
     if (!dtype_ok(kv_dtype)) return DDTV_EUNSUPPORTED;
-    if ((int64_t)vis->B * vis->Q > (int64_t)INT32_MAX) return DDTV_EUNSUPPORTED;
+    if (!grid_fits((int64_t)vis->B * vis->Q, 64)) return DDTV_EUNSUPPORTED;
     AppendArgs p{};
     p.latent = latent;
     p.k_pe = k_pe;

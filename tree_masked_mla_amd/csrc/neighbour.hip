@@ -335,6 +335,7 @@ hipError_t launch_proj(const ProjArgs& p, bool b_trans, int cus, hipStream_t str
     // narrow tiles when wide ones would give fewer workgroups than CUs
     const int64_t wide_wgs = (p.M + kBM - 1) / kBM * ((p.N + Geo<true>::BN - 1) / Geo<true>::BN) * p.H;
     const bool wide = wide_wgs >= cus;
+    (void)hipGetLastError();   // report only this launch's error
     if (b_trans)
         wide ? launch_proj_as<true, true>(p, stream) : launch_proj_as<true, false>(p, stream);
     else
@@ -343,6 +344,7 @@ hipError_t launch_proj(const ProjArgs& p, bool b_trans, int cus, hipStream_t str
 }
 
 hipError_t launch_append_kv(const AppendArgs& p, hipStream_t stream) {
+    (void)hipGetLastError();   // report only this launch's error
     hipLaunchKernelGGL(append_kv_kernel, dim3((unsigned)((int64_t)p.B * p.Q)), dim3(64), 0, stream, p);
     return hipGetLastError();
 }
