@@ -198,6 +198,36 @@ def test_edge_shapes_bf16_mfma(B, H, Q, prefix):
     check_full(w, path=2, what=f"bf16 edge B{B} H{H} Q{Q} P{prefix}")
 
 
+# Batch rows of at most 32 query rows run the matrix kernel in row-half mode: two
+# wave pairs per 16-row group, each over one half of every cache tile, and two
+# partials per split for the merge pass.
+@pytest.mark.parametrize("kv_dtype,path", [(wl.F32, 0), (wl.F32, 2), (wl.BF16, 3), (wl.FP8, 0)])
+@pytest.mark.parametrize("B,H,Q,prefix,split_len", [
+    (2, 16, 1, [1000, 3], 0),          # decode (q_len 1), 16 rows
+    (2, 16, 1, [1000, 3], 256),        # the same over several splits
+    (3, 8, 4, [200, 0, 77], 0),        # 32 rows, tree masks, a row with no prefix
+    (1, 16, 2, [4100], 0),             # 32 rows over a long prefix (planned splits)
+    (2, 5, 5, [63, 64], 128),          # 25 rows: pairs 2, 3 hold rows 16..24
+    (2, 1, 9, [40, 5], 0),             # 9 rows (the matrix path forced below 16)
+])
+def test_row_half_mode(kv_dtype, path, B, H, Q, prefix, split_len):
+    if path == 0 and Q * H < 16:
+        path = 2
+    w = wl.make_workload(f"half{B}x{H}x{Q}", 6000 + B * 100 + H * 10 + Q, B=B, H=H, Q=Q, prefix=prefix,
+                         tree="uniform", kv_dtype=kv_dtype)
+    check_full(w, path=path, split_len=split_len,
+               what=f"row-half B{B} H{H} Q{Q} P{prefix} dtype {kv_dtype} split {split_len}")
+
+
+def test_row_half_mode_single_visible_position_is_exact():
+    """Row-half mode on a lone position: one half holds it (p = 1), the other
+    half is empty (weight 0 in the merge), so the output is the row bit for bit."""
+    w = wl.make_workload("half-single", 6900, B=1, H=16, Q=1, prefix=0, tree="uniform")
+    r, out, lse = run(w, path=2)
+    for h in range(w.H):
+        assert np.array_equal(out[h], w.ckv[0]), h
+
+
 @pytest.mark.parametrize("path", [1, 2])
 def test_single_visible_position_is_exact(path):
     """With no prefix the root sees only itself: p = 1, so the output is its latent row bit for bit."""

@@ -94,6 +94,7 @@ ddtv_status check_vis(const ddtv_vis* vis) {
 struct Plan {
     int path = DDTV_PATH_AUTO;
     bool bf16_mma = false;   // bf16 caches on the bf16 matrix cores
+    bool halves = false;     // row-half mode of the matrix kernel (at most 32 query rows per batch row)
     int rows_per_wg = 0;
     int n_rt = 0;
     int split_len = 0;
@@ -234,8 +235,14 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     // fp32 and FP8 caches run the fp32 matrix-core kernel under either matrix path
     if (p->path == DDTV_PATH_MFMA_F32 && kv_dtype != DDTV_BF16) p->path = DDTV_PATH_MFMA;
     p->bf16_mma = p->path == DDTV_PATH_MFMA && kv_dtype == DDTV_BF16;
-    p->rows_per_wg = p->path == DDTV_PATH_VALU ? kValuRows : (p->bf16_mma ? bf16_rows_per_workgroup() : mfma_rows_per_workgroup(kv_dtype));
     const int64_t R = (int64_t)vis->Q * H;
+    // Batch rows of at most 32 query rows run the fp32 matrix kernel in row-half
+    // mode: two wave pairs share each 16-row group and split every cache tile.
+    p->halves = p->path != DDTV_PATH_VALU && !p->bf16_mma && R <= 32;
+    p->rows_per_wg = p->path == DDTV_PATH_VALU ? kValuRows
+                     : p->bf16_mma             ? bf16_rows_per_workgroup()
+                     : p->halves               ? 32
+                                               : mfma_rows_per_workgroup(kv_dtype);
     if (R > (int64_t)INT32_MAX / 2) return DDTV_EUNSUPPORTED;
     p->n_rt = (int)((R + p->rows_per_wg - 1) / p->rows_per_wg);
     const int max_kv = vis->max_kv;
@@ -313,9 +320,10 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     p->n_split = (max_kv + p->split_len - 1) / p->split_len;
     p->grid = (int64_t)vis->B * p->n_rt * p->n_split;
     if (!grid_fits(p->grid, 512)) return DDTV_EUNSUPPORTED;   // 512 = the largest attention workgroup
-    if (p->n_split > 1 && !grid_fits(((int64_t)vis->B * R + 1) / 2, 256)) return DDTV_EUNSUPPORTED;   // merge
-    if (p->n_split > 1) {
-        const size_t rows_total = (size_t)vis->B * p->n_split * (size_t)R;
+    const int parts = p->n_split * (p->halves ? 2 : 1);   // partials per batch row
+    if (parts > 1 && !grid_fits(((int64_t)vis->B * R + 1) / 2, 256)) return DDTV_EUNSUPPORTED;   // merge
+    if (parts > 1) {
+        const size_t rows_total = (size_t)vis->B * parts * (size_t)R;
         p->ws_part_o = 0;
         p->ws_part_ml = round_up(rows_total * kDLat * sizeof(float), 256);
         p->ws_bytes = p->ws_part_ml + round_up(rows_total * sizeof(float2), 256);
@@ -637,6 +645,7 @@ ddtv_status ddtv_verify_attn_ex(const float* q_abs, const float* q_rope, const v
     a.split_len = p.split_len;
     a.n_split = p.n_split;
     a.spread = p.order == DDTV_ORDER_SPREAD;
+    a.halves = p.halves;
     a.order = a.spread ? vis->order : nullptr;   // XCD-local keeps rows in their natural order
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 
@@ -646,7 +655,7 @@ ddtv_status ddtv_verify_attn_ex(const float* q_abs, const float* q_rope, const v
                                                 : launch_attn_mfma(a, kv_dtype, p.grid, stream);
     if (e != hipSuccess) return DDTV_EDEVICE;
     if (opts && opts->attn_end && hipEventRecord(opts->attn_end, stream) != hipSuccess) return DDTV_EDEVICE;
-    if (p.n_split > 1 && launch_merge(a, stream) != hipSuccess) return DDTV_EDEVICE;
+    if ((p.n_split > 1 || p.halves) && launch_merge(a, stream) != hipSuccess) return DDTV_EDEVICE;
     return DDTV_OK;
 }
 

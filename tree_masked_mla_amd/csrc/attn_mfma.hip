@@ -29,6 +29,14 @@
 //    the query is pre-scaled by scale*log2(e) when it is loaded.
 //  * Online softmax in exp2 units with lazy rescaling (the running max moves only
 //    when a tile beats it by more than 2^8).
+//  * Row-half mode, for batch rows of at most 32 query rows (decode-like shapes,
+//    where the cache stream is the bound): a workgroup owns 32 rows, and wave
+//    pairs 2k and 2k + 1 both own rows 16k .. 16k + 15 but take cache rows 0..15
+//    and 16..31 of every tile respectively, each with its own online softmax.
+//    The two halves leave two partials per split, combined by the merge pass like
+//    any other split.  With 16 rows this puts pairs 0 and 1 (waves 0..3, one per
+//    SIMD) to work where otherwise one pair (two SIMDs) would do all the matrix
+//    work of the tile.
 //  * fp32 caches go HBM->LDS with global_load_lds_dwordx4 (no VGPR staging),
 //    double buffered; bf16 and FP8 caches are widened exactly to fp32 through
 //    VGPRs on the way in.
@@ -220,17 +228,31 @@ __device__ __forceinline__ f32x4 lds16(const char* base, uint32_t off) {
 }
 
 // Partial S^T of the tile at Kb over this wave's half of the contraction (two
-// independent accumulators: cache rows n and 16 + n), stored to the wave's swap
-// area; issue() starts the next tile's loads part-way through.
-template <int HALF, class Issue>
+// independent accumulators: cache rows n and 16 + n; in row-half mode one, cache
+// row 16 rh + n), stored to the wave's swap area; issue() starts the next tile's
+// loads part-way through.
+template <int HALF, bool kHv, class Issue>
 __device__ __forceinline__ void qk_slot(const char* Kb, const TileOffsets& to, const f32x4 (&qreg)[18],
-                                        f32x4* sx_mine, int lane, Issue&& issue) {
+                                        f32x4* sx_mine, int lane, Issue&& issue, int rh) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     auto kchunk = [&](int row_hi, int t) -> f32x4 {
         const int tg = 18 * HALF + t;
         return (tg < 32) ? lds16(Kb, to.qoff[tg & 3] + 256 * (tg >> 2) + row_hi * 32768)
                          : lds16(Kb, to.roff[tg - 32] + row_hi * 4096);
     };
+    if constexpr (kHv) {
+        f32x4 a0 = kchunk(rh, 0);
+#pragma unroll
+        for (int t = 0; t < 18; ++t) {
+            const f32x4 c0 = a0;
+            if (t + 1 < 18) a0 = kchunk(rh, t + 1);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(c0[u], qreg[t][u], s0, 0, 0, 0);
+            if (t == 2) issue();
+        }
+        sx_mine[lane] = s0;
+        return;
+    }
     f32x4 a0 = kchunk(0, 0), a1 = kchunk(1, 0);
 #pragma unroll
     for (int t = 0; t < 18; ++t) {
@@ -257,28 +279,31 @@ __device__ __forceinline__ void qk_slot(const char* Kb, const TileOffsets& to, c
 
 // Full scores of the tile starting at cache position t0 (own partial and the
 // partner's, both from LDS), online softmax, then O += P V over this wave's 256 dims.
-template <int HALF>
+// Row-half mode: only the 16 cache rows of half rh.
+template <int HALF, bool kHv>
 __device__ __forceinline__ void sm_pv_slot(f32x4 (&oacc)[16], const f32x4* sx_mine, const f32x4* sx_partner,
                                            const char* Kb, const TileOffsets& to, float& m_run, float& l_lane,
                                            const uint32_t* mrow, int g, int n, int lane, int t0, int P,
-                                           int kv_hi) {
+                                           int kv_hi, int rh) {
+    constexpr int NE = kHv ? 4 : 8;   // scores per lane: cache rows 16 (e >> 2) + 4g + (e & 3), or 16 rh + 4g + e
     float sv[8];
     {
         const f32x4 a0 = sx_mine[lane] + sx_partner[lane];
-        const f32x4 a1 = sx_mine[64 + lane] + sx_partner[64 + lane];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sv[e] = a0[e];
-            sv[4 + e] = a1[e];
+        for (int e = 0; e < 4; ++e) sv[e] = a0[e];
+        if constexpr (!kHv) {
+            const f32x4 a1 = sx_mine[64 + lane] + sx_partner[64 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[4 + e] = a1[e];
         }
     }
     const bool full = (t0 + kTile <= P) && (t0 + kTile <= kv_hi);
     float tmax = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < NE; ++e) {
         float x = sv[e];
         if (!full) {
-            const int j = t0 + (e >> 2) * 16 + 4 * g + (e & 3);
+            const int j = t0 + (kHv ? rh : (e >> 2)) * 16 + 4 * g + (e & 3);
             bool vis = j < kv_hi;
             if (vis && j >= P) vis = (mrow[(j - P) >> 5] >> ((j - P) & 31)) & 1u;
             x = vis ? x : -INFINITY;
@@ -306,17 +331,18 @@ __device__ __forceinline__ void sm_pv_slot(f32x4 (&oacc)[16], const f32x4* sx_mi
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < NE; ++e) {
         sv[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
         l_lane += sv[e];
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < NE; ++e) {
         const int vr = (e >> 2) * 16 + 4 * g + (e & 3);
         const float pv = sv[e];
         f32x4 vf[4];
 #pragma unroll
-        for (int T = 0; T < 4; ++T) vf[T] = lds16(Kb, to.voff[e & 3] + (e >> 2) * 32768 + 256 * (4 * HALF + T));
+        for (int T = 0; T < 4; ++T)
+            vf[T] = lds16(Kb, to.voff[e & 3] + (kHv ? rh : (e >> 2)) * 32768 + 256 * (4 * HALF + T));
         (void)vr;
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
@@ -328,14 +354,18 @@ __device__ __forceinline__ void sm_pv_slot(f32x4 (&oacc)[16], const f32x4* sx_mi
     }
 }
 
-// One workgroup's work; HALF is the wave's half of the pair (wave-uniform).
-template <int KV, int HALF>
+// One workgroup's work; HALF is the wave's half of the pair (wave-uniform);
+// kHv selects row-half mode.
+template <int KV, int HALF, bool kHv>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, int s, int rt, int wave,
                                           int lane) {
     const int tid = wave * 64 + lane;
     const int g = lane >> 4;     // lane group
     const int n = lane & 15;     // query row (score layout) within the pair's 16
     const int pair = wave >> 1;
+    constexpr int kRowsWG = kHv ? 32 : kRows;      // query rows per workgroup
+    const int rgrp = kHv ? (pair >> 1) : pair;     // the pair's 16-row group
+    const int rh = kHv ? (pair & 1) : 0;           // row-half mode: the pair's half of each tile
 
     const ddtv_row rowd = a.rows[b];
     const int kv_len = rowd.kv_len, P = rowd.prefix;
@@ -354,7 +384,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
     // Query half: register t holds dims 16(18*HALF + t) + 4g .. +3 of row n (this
     // permutation of the contraction index matches the cache-operand reads),
     // pre-multiplied by scale*log2(e) so the scores come out in exp2 units.
-    const int myrow = rt * kRows + pair * 16 + n;
+    const int myrow = rt * kRowsWG + rgrp * 16 + n;
     const bool row_ok = myrow < a.R;
     // The 18 loads are unconditional (a row past the end reads row 0 and scales it
     // by 0), so they issue back to back under one wait; a per-load row test made
@@ -389,7 +419,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
     // trees, few heads) only loads its share of the tiles and meets the barriers:
     // its matrix work would be discarded, and skipping it frees the SIMDs for the
     // pairs with rows.  (A separate loop, so the main loop's code is unchanged.)
-    if (rt * kRows + pair * 16 >= a.R) {
+    if (rt * kRowsWG + rgrp * 16 >= a.R) {
         for (int it = 0; it < ntiles; ++it) {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -418,10 +448,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
             }
         };
         const char* Kb = reinterpret_cast<const char*>(sm.kv[it & 1]);
-        qk_slot<HALF>(Kb, to, qreg, sx_mine, lane, issue);
+        qk_slot<HALF, kHv>(Kb, to, qreg, sx_mine, lane, issue, rh);
         __syncthreads();                                  // partner's partial scores are in LDS
-        sm_pv_slot<HALF>(oacc, sx_mine, sx_partner, Kb, to, m_run, l_lane, mrow, g, n, lane, kv_lo + it * kTile, P,
-                         kv_hi);
+        sm_pv_slot<HALF, kHv>(oacc, sx_mine, sx_partner, Kb, to, m_run, l_lane, mrow, g, n, lane, kv_lo + it * kTile,
+                              P, kv_hi, rh);
         if (KV != DDTV_F32 && more) store_tile_narrow<KV>(sm.kv[(it + 1) & 1], stage, tid);
     }
 
@@ -429,8 +459,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
     float l_row = l_lane + wave_xor(l_lane, 16);
     l_row += wave_xor(l_row, 32);
     const float kLn2 = 0.69314718055994530942f;
-    const int orow_base = rt * kRows + pair * 16 + 4 * g;
-    if (n_b == 1) {
+    const int orow_base = rt * kRowsWG + rgrp * 16 + 4 * g;
+    if (!kHv && n_b == 1) {
         const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -447,7 +477,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         if (HALF == 0 && a.lse && g == 0 && row_ok)
             a.lse[(int64_t)b * a.R + myrow] = l_row > 0.f ? (m_run + log2f(l_row)) * kLn2 : -INFINITY;
     } else {
-        const int64_t pbase = ((int64_t)b * a.n_split + s) * a.R;
+        // partial entry of this split (row-half mode: two per split, one per half)
+        const int64_t pbase = kHv ? ((int64_t)b * 2 * a.n_split + 2 * s + rh) * a.R
+                                  : ((int64_t)b * a.n_split + s) * a.R;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int orow = orow_base + j;
@@ -463,7 +495,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
     }
 }
 
-template <int KV>
+// kHv: row-half mode (its own kernel, so the code of the usual mode is unchanged).
+template <int KV, bool kHv>
 __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs a) {
     __shared__ Smem sm;
     const int64_t w = work_item(a);
@@ -475,9 +508,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (wave & 1)
-        attn_body<KV, 1>(a, sm, b, s, rt, wave, lane);
+        attn_body<KV, 1, kHv>(a, sm, b, s, rt, wave, lane);
     else
-        attn_body<KV, 0>(a, sm, b, s, rt, wave, lane);
+        attn_body<KV, 0, kHv>(a, sm, b, s, rt, wave, lane);
+}
+
+template <int KV>
+void launch_kv(const AttnArgs& a, int64_t grid, hipStream_t stream) {
+    if (a.halves)
+        hipLaunchKernelGGL((attn_mfma_kernel<KV, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((attn_mfma_kernel<KV, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
 }
 
 }  // namespace
@@ -487,11 +528,11 @@ int mfma_rows_per_workgroup(int /*kv_dtype*/) { return kRows; }
 hipError_t launch_attn_mfma(const AttnArgs& a, int kv_dtype, int64_t grid, hipStream_t stream) {
     (void)hipGetLastError();   // report only this launch's error
     if (kv_dtype == DDTV_BF16)
-        hipLaunchKernelGGL(attn_mfma_kernel<DDTV_BF16>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+        launch_kv<DDTV_BF16>(a, grid, stream);
     else if (kv_dtype == DDTV_FP8_E4M3)
-        hipLaunchKernelGGL(attn_mfma_kernel<DDTV_FP8_E4M3>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+        launch_kv<DDTV_FP8_E4M3>(a, grid, stream);
     else
-        hipLaunchKernelGGL(attn_mfma_kernel<DDTV_F32>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+        launch_kv<DDTV_F32>(a, grid, stream);
     return hipGetLastError();
 }
 

@@ -10,7 +10,8 @@
 //
 // 128 threads per query row (one float4 of the 512-d output each), 2 rows per
 // workgroup.  Rows whose batch row needed a single split were finished by the
-// attention kernel and are skipped.  The splits are read in batches of kBatch
+// attention kernel and are skipped (except in row-half mode, where every split
+// leaves two partials).  The splits are read in batches of kBatch
 // independent loads and folded in with an online rescale (the running maximum
 // moves batch by batch), so up to kBatch splits cost one memory round trip.
 #include "ddtv_internal.hpp"
@@ -28,10 +29,11 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
     const int b = (int)(gr / a.R);
     const int row = (int)(gr - (int64_t)b * a.R);
     const int kv_len = a.rows[b].kv_len;
-    const int n_b = (kv_len + a.split_len - 1) / a.split_len;
+    const int hm = a.halves ? 2 : 1;                   // partials per split
+    const int n_b = hm * ((kv_len + a.split_len - 1) / a.split_len);
     if (n_b <= 1) return;
     const int c = threadIdx.x & 127;
-    const int64_t pbase = (int64_t)b * a.n_split * a.R + row;   // split s at pbase + s * R
+    const int64_t pbase = (int64_t)b * hm * a.n_split * a.R + row;   // partial s at pbase + s * R
     const float4* po = reinterpret_cast<const float4*>(a.part_o);
 
     float M = -INFINITY, L = 0.f;
