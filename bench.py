@@ -39,6 +39,21 @@ KERNEL_SOURCES = {
 }
 
 
+def roofline_bound(valu, flops, nbytes, kernel_ms, peak_tflops):
+    """The roofline that binds the attention kernel: the larger of its compute
+    floor (flops at the matrix or vector peak) and its memory floor (algorithmic
+    bytes at the HBM peak).  The tree workloads are compute-bound; decode-shaped
+    rows (q_len 1) carry ~15 flops per byte and are HBM-bound."""
+    t = kernel_ms / 1e3
+    if nbytes / (HBM_PEAK_GBPS * 1e9) > flops / (peak_tflops * 1e12):
+        gbps = nbytes / t / 1e9
+        return {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    tflops = flops / t / 1e12
+    return {"bound": "alu" if valu else "mfma", "achieved": round(tflops, 3), "peak": peak_tflops,
+            "unit": "TFLOP/s", "frac": round(tflops / peak_tflops, 4)}
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -503,11 +518,7 @@ def main():
         "step_us": round(ms_step * 1e3, 2),
         "host_wall_ms_per_step": round((t_host1 - t_host0) * 1e3 / K, 4),
         "roofline": {
-            "bound": "alu" if path == dd.DDTV_PATH_VALU else "mfma",
-            "achieved": round(achieved_tflops, 3),
-            "peak": PEAK_TFLOPS[peak_key],
-            "unit": "TFLOP/s",
-            "frac": round(achieved_tflops / PEAK_TFLOPS[peak_key], 4),
+            **roofline_bound(path == dd.DDTV_PATH_VALU, flops, nbytes, attn_avg_ms, PEAK_TFLOPS[peak_key]),
             "traffic": traffic,
             "kernel": kernel,
             "flops_per_launch": flops,
