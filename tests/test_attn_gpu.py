@@ -325,6 +325,23 @@ def test_c4_full_sampled():
     _full_sampled("c4", 64)
 
 
+def test_c4_decode_shape_row_half_full_sampled():
+    """c4 sizes at q_len 1 (16 query rows per batch row, 262,152 cache rows): the
+    row-half mode in the launch the decode probe times (32 splits, two partials
+    each, merged), on every query row of two batch rows against the oracle."""
+    say("generate c4 at q_len 1")
+    w = wl.config("c4", Q=1)
+    bits, _, _ = oracle.build_visibility(w.parent)
+    r, out, lse = run(w)
+    say(f"  plan {r.plan()}")
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    rows = np.concatenate([np.arange(0, 16), np.arange(7 * 16, 8 * 16)]).astype(np.int64)
+    ref, rlse = oracle_rows(w, bits, rows, chunk=4)
+    e = assert_close(out[rows], ref, 0, "c4 q_len 1")
+    assert_lse_close(lse[rows], rlse, 0, "c4 q_len 1")
+    say(f"  c4 q_len 1: max abs err {e:.2e} on {len(rows)} rows")
+
+
 def test_c5_full_sampled():
     _full_sampled("c5", 32)
 
