@@ -271,8 +271,22 @@ def test_plan_rules(lib):
     rc, p_, L, ns, wg, order = dd.ddtv_plan_info(vis, 16, dd.DDTV_BF16)
     rows = 2 * ns * 16                                   # one partial per split
     assert rc == 0 and dd.ddtv_workspace_bytes(vis, 16, dd.DDTV_BF16) == (ru(rows * 2048) + ru(rows * 8) if ns > 1 else 0)
-    vis = fake_vis(B=2, Q=3, prefix=(1000, 3))          # 33 rows: the usual 64-row mode
-    assert dd.ddtv_plan_info(vis, 11, 0)[0] == 0 and dd.ddtv_plan_info(vis, 11, 0, dd.make_opts(split_len=0))[3] >= 1
+    # 33 rows: the usual 64-row mode, one partial per split (none with a single split)
+    vis = fake_vis(B=2, Q=3, prefix=(1000, 3))
+    for L in (0, 128, 2048):
+        opts = dd.make_opts(split_len=L)
+        rc, p_, L_, ns, wg, order = dd.ddtv_plan_info(vis, 11, 0, opts)
+        rows = 2 * ns * 33
+        want = ru(rows * 2048) + ru(rows * 8) if ns > 1 else 0
+        assert rc == 0 and wg == 2 * ns and dd.ddtv_workspace_bytes(vis, 11, 0, opts) == want, (L, ns)
+    # 32 rows on the same trees: row-half mode, two partials per split even with a single split
+    vis32 = fake_vis(B=2, Q=2, prefix=(1000, 3))
+    for L in (128, 2048):
+        opts = dd.make_opts(split_len=L)
+        rc, p_, L_, ns, wg, order = dd.ddtv_plan_info(vis32, 16, 0, opts)
+        rows = 2 * 2 * ns * 32
+        assert rc == 0 and wg == 2 * ns, (L, ns, wg)
+        assert dd.ddtv_workspace_bytes(vis32, 16, 0, opts) == ru(rows * 2048) + ru(rows * 8), (L, ns)
     # a grid past 2^32 work-items is refused before any launch
     big = fake_vis(B=(1 << 16) + 1, Q=256, prefix=np.zeros((1 << 16) + 1, np.int32))
     assert dd.ddtv_plan_info(big, 128, 0)[0] == dd.DDTV_EUNSUPPORTED
