@@ -28,10 +28,12 @@
  *     DDTV_EDEVICE.  No exception crosses this interface.
  *   - Device pointers to float data must be 16-byte aligned.
  *   - Calls are re-entrant and thread-safe; calls on different streams may overlap
- *     (each with its own output and workspace buffers).  The only state kept is a
- *     small cache of split plans (keyed by shapes, options, CU count and prefix
- *     lengths, guarded by a lock) and the per-device CU count; neither changes
- *     results.
+ *     (each with its own output and workspace buffers), except
+ *     ddtv_verify_attn_noalloc, whose calls share one scratch per GPU.  The only
+ *     state kept is a small cache of split plans (keyed by shapes, options, CU
+ *     count, prefix lengths and workspace limit, guarded by a lock), the
+ *     per-device CU count and the per-device address of that scratch; none of
+ *     them changes results.
  */
 #ifndef DDTV_H
 #define DDTV_H
@@ -258,6 +260,30 @@ ddtv_status ddtv_verify_attn_ex(const float *q_abs, const float *q_rope, const v
                                 const ddtv_vis *vis, float scale, float *out, float *lse,
                                 void *workspace, size_t workspace_bytes, hipStream_t stream,
                                 const ddtv_opts *opts);
+
+/*
+ * ddtv_verify_attn_ex without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  It calls no hipMalloc, hipFree or other
+ * allocating routine.  The split partials go to a scratch array that the library
+ * holds in each GPU's memory (DDTV_NOALLOC_SCRATCH_BYTES per GPU, kept until the
+ * process ends); the caller still passes inputs and outputs.
+ *   Arguments, results and other errors: as ddtv_verify_attn_ex.  The automatic
+ *   split choice only considers plans whose partials fit the scratch, so its
+ *   plan may have fewer KV splits than ddtv_verify_attn_ex picks for the same
+ *   call.  DDTV_EWORKSPACE: even the plan with the fewest splits (or the forced
+ *   split length in opts) needs more than DDTV_NOALLOC_SCRATCH_BYTES; nothing is
+ *   enqueued then.  DDTV_EDEVICE also covers a failed lookup of the scratch.
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap in time on
+ *   one GPU (several streams or host threads) race on it and must be serialised
+ *   by the caller.  Each call writes every partial it reads, so nothing carries
+ *   over from the previous call.
+ */
+#define DDTV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+ddtv_status ddtv_verify_attn_noalloc(const float *q_abs, const float *q_rope, const void *ckv,
+                                     const void *k_rope, ddtv_dtype kv_dtype, int32_t H,
+                                     const ddtv_vis *vis, float scale, float *out, float *lse,
+                                     hipStream_t stream, const ddtv_opts *opts);
 
 /*
  * External-prefix mode: the caller brings each query row's attention over the

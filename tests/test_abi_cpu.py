@@ -415,3 +415,24 @@ int main(void) {
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, (r.returncode, r.stderr)
     assert int(r.stdout.strip()) == dd.ddtv_version()
+
+
+def test_noalloc_host_errors(lib):
+    """ddtv_verify_attn_noalloc checks its arguments like ddtv_verify_attn_ex and
+    refuses, before any HIP call, a plan whose partials exceed the scratch."""
+    vis = fake_vis(B=2, Q=64, prefix=(20000, 3000))
+    E = dd.DDTV_EINVAL
+
+    def call(q_abs=FAKE, out=FAKE, scale=0.07, H=16, opts=None):
+        return lib.ddtv_verify_attn_noalloc(q_abs, FAKE, FAKE, FAKE, 0, H, ctypes.byref(vis.vis),
+                                            ctypes.c_float(scale), out, None, None,
+                                            ctypes.byref(opts) if opts is not None else None)
+    assert call(q_abs=None) == E
+    assert call(out=FAKE + 4) == E
+    assert call(scale=float("nan")) == E
+    assert call(H=0) == E
+    assert call(opts=dd.make_opts(split_len=100)) == E
+    # 32-position splits: 626 splits x 2 batch rows x 1024 query rows of partials, far past the scratch
+    assert call(opts=dd.make_opts(split_len=32)) == dd.DDTV_EWORKSPACE
+    need = dd.ddtv_workspace_bytes(vis, 16, 0, dd.make_opts(split_len=32))
+    assert need > dd.NOALLOC_SCRATCH_BYTES

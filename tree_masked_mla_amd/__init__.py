@@ -23,13 +23,14 @@ DDTV_F32, DDTV_BF16, DDTV_FP8_E4M3 = 0, 1, 2
 DDTV_PATH_AUTO, DDTV_PATH_VALU, DDTV_PATH_MFMA, DDTV_PATH_MFMA_F32 = 0, 1, 2, 3
 DDTV_ORDER_AUTO, DDTV_ORDER_XCD_LOCAL, DDTV_ORDER_SPREAD = 0, 1, 2
 D_LATENT, D_ROPE, MAX_Q = 512, 64, 256
+NOALLOC_SCRATCH_BYTES = 32 << 20   # DDTV_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = (
     "ddtv_vis_bytes", "ddtv_build_visibility", "ddtv_read_status", "ddtv_workspace_bytes",
     "ddtv_workspace_bytes_ex", "ddtv_verify_attn", "ddtv_verify_attn_ex", "ddtv_plan_info",
     "ddtv_status_string", "ddtv_version", "ddtv_build_tree", "ddtv_tree_accept",
     "ddtv_tail_workspace_bytes", "ddtv_verify_attn_tail", "ddtv_prepare_query", "ddtv_value_proj",
-    "ddtv_append_kv",
+    "ddtv_append_kv", "ddtv_verify_attn_noalloc",
 )
 
 
@@ -82,6 +83,8 @@ def load(path: str = LIB_PATH):
     lib.ddtv_verify_attn.restype = ctypes.c_int
     lib.ddtv_verify_attn_ex.argtypes = [P, P, P, P, ctypes.c_int, i32, VP, ctypes.c_float, P, P, P, sz, P, OP]
     lib.ddtv_verify_attn_ex.restype = ctypes.c_int
+    lib.ddtv_verify_attn_noalloc.argtypes = [P, P, P, P, ctypes.c_int, i32, VP, ctypes.c_float, P, P, P, OP]
+    lib.ddtv_verify_attn_noalloc.restype = ctypes.c_int
     lib.ddtv_plan_info.argtypes = [VP, i32, ctypes.c_int, OP, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                    ctypes.POINTER(i32), ctypes.POINTER(i64), ctypes.POINTER(i32)]
     lib.ddtv_plan_info.restype = ctypes.c_int
@@ -248,6 +251,15 @@ def ddtv_verify_attn(q_abs, q_rope, ckv, k_rope, kv_dtype: int, H: int, vis: Vis
     if opts is None:
         return lib.ddtv_verify_attn(*args)
     return lib.ddtv_verify_attn_ex(*args, ctypes.byref(opts))
+
+
+def ddtv_verify_attn_noalloc(q_abs, q_rope, ckv, k_rope, kv_dtype: int, H: int, vis: Visibility, scale: float,
+                             out, lse=None, stream=None, opts: ddtv_opts | None = None) -> int:
+    """ddtv_verify_attn_ex without a workspace: split partials go to the library's
+    per-GPU scratch (DDTV_NOALLOC_SCRATCH_BYTES)."""
+    return load().ddtv_verify_attn_noalloc(_ptr(q_abs), _ptr(q_rope), _ptr(ckv), _ptr(k_rope), kv_dtype, H,
+                                           ctypes.byref(vis.vis), ctypes.c_float(scale), _ptr(out), _ptr(lse),
+                                           _stream(stream), ctypes.byref(opts) if opts is not None else None)
 
 
 def ddtv_prepare_query(q, w_kc, vis: Visibility, q_abs, q_rope, rope_theta: float, positions=None,

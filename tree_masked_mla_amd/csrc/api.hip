@@ -147,7 +147,7 @@ double estimate(const std::vector<int>& kv, int n_rt, int L, int cus, double set
 }
 
 ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const ddtv_opts* opts,
-                               Plan* p);
+                               size_t ws_cap, Plan* p);
 
 // Plans are pure functions of the shapes, the options, the device's CU count and
 // the per-row cache lengths; a verify loop re-plans the same shapes every step, so
@@ -157,6 +157,7 @@ struct PlanKey {
     int32_t B, Q, W, max_kv, H, dtype, path, split, order, has_order, cus;
     int64_t total_kv;
     uint64_t prefix_hash;
+    uint64_t ws_cap;
     bool operator==(const PlanKey& o) const { return memcmp(this, &o, sizeof *this) == 0; }
 };
 
@@ -170,7 +171,10 @@ uint64_t hash_prefix(const ddtv_vis* vis) {
     return h;
 }
 
-ddtv_status make_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const ddtv_opts* opts, Plan* p) {
+// ws_cap: the largest workspace the caller can offer (SIZE_MAX: any); split
+// candidates whose partials would not fit are skipped.
+ddtv_status make_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const ddtv_opts* opts, Plan* p,
+                      size_t ws_cap = SIZE_MAX) {
     ddtv_status st = check_vis(vis);
     if (st) return st;
     PlanKey key;
@@ -188,6 +192,7 @@ ddtv_status make_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const
     key.has_order = vis->order != nullptr;
     key.cus = cu_count();
     key.prefix_hash = hash_prefix(vis);
+    key.ws_cap = ws_cap;
     static std::mutex mu;
     static PlanKey keys[8];
     static Plan plans[8];
@@ -200,7 +205,7 @@ ddtv_status make_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const
                 return DDTV_OK;
             }
     }
-    st = make_plan_uncached(vis, H, kv_dtype, opts, p);
+    st = make_plan_uncached(vis, H, kv_dtype, opts, ws_cap, p);
     if (st) return st;
     std::lock_guard<std::mutex> lock(mu);
     keys[next] = key;
@@ -210,8 +215,16 @@ ddtv_status make_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const
     return DDTV_OK;
 }
 
+// Workspace bytes for `parts` partials per batch row of R query rows (0 when a
+// single partial per row means the attention kernel writes the output itself).
+size_t partial_bytes(int B, int64_t R, int parts) {
+    if (parts <= 1) return 0;
+    const size_t rows_total = (size_t)B * parts * (size_t)R;
+    return round_up(rows_total * kDLat * sizeof(float), 256) + round_up(rows_total * sizeof(float2), 256);
+}
+
 ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const ddtv_opts* opts,
-                               Plan* p) {
+                               size_t ws_cap, Plan* p) {
     ddtv_status st = check_vis(vis);
     if (st) return st;
     if (H < 1 || H > 65536) return DDTV_EINVAL;
@@ -302,6 +315,8 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
             int64_t wgs = 0;
             for (int b = 0; b < vis->B; ++b) wgs += (int64_t)((kv[b] + L - 1) / L) * p->n_rt;
             if (wgs > wg_cap && S > 1) break;
+            const int parts_L = ((max_kv + L - 1) / L) * (p->halves ? 2 : 1);
+            if (S > 1 && partial_bytes(vis->B, R, parts_L) > ws_cap) break;   // more splits only need more
             int order = DDTV_ORDER_XCD_LOCAL;
             const double e = cost_at(L, &order);
             if (e < best * 0.98) {   // prefer fewer splits unless clearly better
@@ -322,14 +337,9 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     if (!grid_fits(p->grid, 512)) return DDTV_EUNSUPPORTED;   // 512 = the largest attention workgroup
     const int parts = p->n_split * (p->halves ? 2 : 1);   // partials per batch row
     if (parts > 1 && !grid_fits(((int64_t)vis->B * R + 1) / 2, 256)) return DDTV_EUNSUPPORTED;   // merge
-    if (parts > 1) {
-        const size_t rows_total = (size_t)vis->B * parts * (size_t)R;
-        p->ws_part_o = 0;
-        p->ws_part_ml = round_up(rows_total * kDLat * sizeof(float), 256);
-        p->ws_bytes = p->ws_part_ml + round_up(rows_total * sizeof(float2), 256);
-    } else {
-        p->ws_bytes = 0;
-    }
+    p->ws_part_o = 0;
+    p->ws_part_ml = parts > 1 ? round_up((size_t)vis->B * parts * (size_t)R * kDLat * sizeof(float), 256) : 0;
+    p->ws_bytes = partial_bytes(vis->B, R, parts);
     return DDTV_OK;
 }
 
@@ -365,6 +375,79 @@ ddtv_status tail_plan(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const
     L->plan = L->lse + round_up((size_t)vis->B * vis->Q * (size_t)H * sizeof(float), 256);
     L->total = L->plan + p->ws_bytes;
     return DDTV_OK;
+}
+
+ddtv_status check_verify_args(const float* q_abs, const float* q_rope, const void* ckv, const void* k_rope,
+                              const float* out, const float* lse, float scale) {
+    if (!q_abs || !q_rope || !ckv || !k_rope || !out) return DDTV_EINVAL;
+    if (!aligned(q_abs, 16) || !aligned(q_rope, 16) || !aligned(ckv, 16) || !aligned(k_rope, 16) ||
+        !aligned(out, 16) || (lse && !aligned(lse, 4)))
+        return DDTV_EINVAL;
+    if (!std::isfinite(scale)) return DDTV_EINVAL;
+    return DDTV_OK;
+}
+
+// Enqueue S2..S7 under plan p; `workspace` holds p.ws_bytes of device memory.
+ddtv_status launch_verify(const Plan& p, const float* q_abs, const float* q_rope, const void* ckv,
+                          const void* k_rope, ddtv_dtype kv_dtype, int32_t H, const ddtv_vis* vis, float scale,
+                          float* out, float* lse, void* workspace, hipStream_t stream, const ddtv_opts* opts) {
+    AttnArgs a;
+    a.q_abs = q_abs;
+    a.q_rope = q_rope;
+    a.ckv = ckv;
+    a.k_rope = k_rope;
+    a.bits = vis->bits;
+    a.rows = vis->rows;
+    a.out = out;
+    a.lse = lse;
+    a.part_o = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_part_o) : nullptr;
+    a.part_ml = p.ws_bytes ? reinterpret_cast<float2*>(static_cast<char*>(workspace) + p.ws_part_ml) : nullptr;
+    a.B = vis->B;
+    a.Q = vis->Q;
+    a.H = H;
+    a.W = vis->W;
+    a.R = vis->Q * H;
+    a.n_rt = p.n_rt;
+    a.split_len = p.split_len;
+    a.n_split = p.n_split;
+    a.spread = p.order == DDTV_ORDER_SPREAD;
+    a.halves = p.halves;
+    a.order = a.spread ? vis->order : nullptr;   // XCD-local keeps rows in their natural order
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+
+    if (opts && opts->attn_begin && hipEventRecord(opts->attn_begin, stream) != hipSuccess) return DDTV_EDEVICE;
+    hipError_t e = p.bf16_mma ? launch_attn_mfma_bf16(a, p.grid, stream)
+                   : (p.path == DDTV_PATH_VALU) ? launch_attn_valu(a, kv_dtype, p.grid, stream)
+                                                : launch_attn_mfma(a, kv_dtype, p.grid, stream);
+    if (e != hipSuccess) return DDTV_EDEVICE;
+    if (opts && opts->attn_end && hipEventRecord(opts->attn_end, stream) != hipSuccess) return DDTV_EDEVICE;
+    if ((p.n_split > 1 || p.halves) && launch_merge(a, stream) != hipSuccess) return DDTV_EDEVICE;
+    return DDTV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of ddtv_verify_attn_noalloc: the split partials of callers that cannot
+// allocate a workspace.  Every GPU the library runs on holds one copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, so kernels
+// and copies get the device address looked up below, never the name itself.
+constexpr size_t kScratchBytes = DDTV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of the current device's copy of `scratch`, looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails.
+void* scratch_address() {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        addr[dev] = ptr;
+    }
+    return addr[dev];
 }
 
 }  // namespace
@@ -612,51 +695,30 @@ ddtv_status ddtv_verify_attn_ex(const float* q_abs, const float* q_rope, const v
                                 ddtv_dtype kv_dtype, int32_t H, const ddtv_vis* vis, float scale, float* out,
                                 float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream,
                                 const ddtv_opts* opts) {
-    if (!q_abs || !q_rope || !ckv || !k_rope || !out) return DDTV_EINVAL;
-    if (!aligned(q_abs, 16) || !aligned(q_rope, 16) || !aligned(ckv, 16) || !aligned(k_rope, 16) ||
-        !aligned(out, 16) || (lse && !aligned(lse, 4)))
-        return DDTV_EINVAL;
-    if (!isfinite(scale)) return DDTV_EINVAL;
+    ddtv_status st = check_verify_args(q_abs, q_rope, ckv, k_rope, out, lse, scale);
+    if (st) return st;
     Plan p;
-    ddtv_status st = make_plan(vis, H, kv_dtype, opts, &p);
+    st = make_plan(vis, H, kv_dtype, opts, &p);
     if (st) return st;
     if (p.ws_bytes > 0) {
         if (!workspace || workspace_bytes < p.ws_bytes) return DDTV_EWORKSPACE;
         if (!aligned(workspace, 256)) return DDTV_EINVAL;
     }
+    return launch_verify(p, q_abs, q_rope, ckv, k_rope, kv_dtype, H, vis, scale, out, lse, workspace, stream, opts);
+}
 
-    AttnArgs a;
-    a.q_abs = q_abs;
-    a.q_rope = q_rope;
-    a.ckv = ckv;
-    a.k_rope = k_rope;
-    a.bits = vis->bits;
-    a.rows = vis->rows;
-    a.out = out;
-    a.lse = lse;
-    a.part_o = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_part_o) : nullptr;
-    a.part_ml = p.ws_bytes ? reinterpret_cast<float2*>(static_cast<char*>(workspace) + p.ws_part_ml) : nullptr;
-    a.B = vis->B;
-    a.Q = vis->Q;
-    a.H = H;
-    a.W = vis->W;
-    a.R = vis->Q * H;
-    a.n_rt = p.n_rt;
-    a.split_len = p.split_len;
-    a.n_split = p.n_split;
-    a.spread = p.order == DDTV_ORDER_SPREAD;
-    a.halves = p.halves;
-    a.order = a.spread ? vis->order : nullptr;   // XCD-local keeps rows in their natural order
-    a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
-
-    if (opts && opts->attn_begin && hipEventRecord(opts->attn_begin, stream) != hipSuccess) return DDTV_EDEVICE;
-    hipError_t e = p.bf16_mma ? launch_attn_mfma_bf16(a, p.grid, stream)
-                   : (p.path == DDTV_PATH_VALU) ? launch_attn_valu(a, kv_dtype, p.grid, stream)
-                                                : launch_attn_mfma(a, kv_dtype, p.grid, stream);
-    if (e != hipSuccess) return DDTV_EDEVICE;
-    if (opts && opts->attn_end && hipEventRecord(opts->attn_end, stream) != hipSuccess) return DDTV_EDEVICE;
-    if ((p.n_split > 1 || p.halves) && launch_merge(a, stream) != hipSuccess) return DDTV_EDEVICE;
-    return DDTV_OK;
+ddtv_status ddtv_verify_attn_noalloc(const float* q_abs, const float* q_rope, const void* ckv, const void* k_rope,
+                                     ddtv_dtype kv_dtype, int32_t H, const ddtv_vis* vis, float scale, float* out,
+                                     float* lse, hipStream_t stream, const ddtv_opts* opts) {
+    ddtv_status st = check_verify_args(q_abs, q_rope, ckv, k_rope, out, lse, scale);
+    if (st) return st;
+    Plan p;
+    st = make_plan(vis, H, kv_dtype, opts, &p, kScratchBytes);
+    if (st) return st;
+    if (p.ws_bytes > kScratchBytes) return DDTV_EWORKSPACE;   // the plan's partials do not fit the scratch
+    void* ws = nullptr;
+    if (p.ws_bytes > 0 && !(ws = scratch_address())) return DDTV_EDEVICE;
+    return launch_verify(p, q_abs, q_rope, ckv, k_rope, kv_dtype, H, vis, scale, out, lse, ws, stream, opts);
 }
 
 ddtv_status ddtv_prepare_query(const float* q, int32_t d_nope, int32_t H, const ddtv_vis* vis,
