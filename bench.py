@@ -160,7 +160,7 @@ def time_tree_builder(dd, hip, stream, dev, B, Q, D=12, K=4, steps=20, warmup=3)
     us = hip.elapsed_ms(e0, e1) * 1e3 / steps
     return {"workload": f"B={B} trees of Q={Q} nodes, depth <= {D}, top-{K} per depth (synthetic drafter)",
             "us_per_launch": round(us, 2), "ns_per_node": round(us * 1e3 / Q, 1), "launches": steps,
-            "note": "one wave per tree, one node per step: bound by the dependent chain of Q steps"}
+            "note": "one workgroup per tree: depth-by-depth selection of the Q-1 best lattice nodes (one node per step on ties or positive log-probs)"}
 
 
 def time_tree_accept(dd, hip, stream, r, V=32768, steps=20, warmup=3):

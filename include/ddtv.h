@@ -115,13 +115,14 @@ size_t ddtv_vis_bytes(int32_t B, int32_t Q);
  *   Speculative Decoding", section "Context: Building a Native DDTree Inference
  *   Engine" (a GPU best-first tree builder in place of a per-request CPU heap).
  *   The pages give no rule beyond "best first"; the one implemented is:
- *   - depth d = 1..D offers K choices, logp[b][d-1][0..K-1], sorted in descending
- *     order (unsorted input still gives a valid tree, built by the same steps);
+ *   - depth d = 1..D offers K choices, logp[b][d-1][0..K-1], in any order; a
+ *     choice's rank is its place among them by descending log-probability,
+ *     equal values by index k;
  *   - a node's score is its parent's score plus its choice's log-probability,
  *     summed in float32; the root (node 0) scores 0;
- *   - the next node is the untaken candidate with the highest score; equal scores
- *     go to the candidate whose parent was taken first, then to the better rank.
- *     That is best-first over every child of every taken node.
+ *   - the next node is the untaken candidate with the highest score, over every
+ *     child of every taken node; equal scores go to the candidate whose parent
+ *     was taken first, then to the better rank.
  *   Node i's parent precedes it (parent[b][0] = -1), as ddtv_build_visibility requires.
  *
  *   logp    DEVICE float [B][D][K], finite
@@ -131,12 +132,13 @@ size_t ddtv_vis_bytes(int32_t B, int32_t Q);
  *   K       1..64 choices per depth
  *   parent  DEVICE int32 [B][Q] out: parent node index, -1 for the root
  *   depth, rank, token  DEVICE int32 [B][Q] out or NULL: depth (root 0), choice
- *           rank (root -1), token id (root -1; the rank when tokens is NULL)
+ *           rank (root -1), token id (root -1; tokens[b][d-1][k] for choice k, or
+ *           k itself when tokens is NULL)
  *   score   DEVICE float [B][Q] out or NULL: cumulative log-probability
  * Nodes come out in the order they were taken, so scores are non-increasing when
- * the input is sorted.  Errors: DDTV_EINVAL (null logp or parent, misaligned
- * pointers, B < 1, D < 1, Q outside 1..DDTV_MAX_Q, Q beyond the depth-D tree),
- * DDTV_EUNSUPPORTED (K outside 1..64, B above 2^26), DDTV_EDEVICE.
+ * every log-probability is <= 0.  Errors: DDTV_EINVAL (null logp or parent,
+ * misaligned pointers, B < 1, D < 1, Q outside 1..DDTV_MAX_Q, Q beyond the depth-D
+ * tree), DDTV_EUNSUPPORTED (K outside 1..64, B above 2^26), DDTV_EDEVICE.
  */
 ddtv_status ddtv_build_tree(const float *logp, const int32_t *tokens, int32_t B, int32_t D, int32_t K,
                             int32_t Q, int32_t *parent, int32_t *depth, int32_t *rank, int32_t *token,

@@ -76,17 +76,25 @@ PINS = [
 
 # Mistakes planted in the best-first tree builder's oracle.
 TREE_MUTATIONS = [
-    ("sibling_scored_from_itself", "float s = node_score[c.parent] + logp[(c.depth - 1) * K + c.rank + 1];",
-     "float s = c.score + logp[(c.depth - 1) * K + c.rank + 1];"),
-    ("child_reads_wrong_depth", "float s = c.score + logp[c.depth * K + 0];",
-     "float s = c.score + logp[(c.depth > 0 ? c.depth - 1 : 0) * K + 0];"),
+    ("child_reads_wrong_depth", "float s = c.score + logp[c.depth * K + k];",
+     "float s = c.score + logp[(c.depth > 0 ? c.depth - 1 : 0) * K + k];"),
     ("worst_first", "if (a->score != b->score) return a->score > b->score;",
      "if (a->score != b->score) return a->score < b->score;"),
     ("ties_later_parent_first", "if (a->parent != b->parent) return a->parent < b->parent;",
      "if (a->parent != b->parent) return a->parent > b->parent;"),
-    ("siblings_skip_last", "if (c.depth >= 1 && c.rank + 1 < K) {", "if (c.depth >= 1 && c.rank + 2 < K) {"),
+    ("ties_worse_rank_first", "return a->rank < b->rank;", "return a->rank > b->rank;"),
+    ("choices_skip_last", "for (int k = 0; k < K; ++k) {\n                float s",
+     "for (int k = 0; k < K - 1; ++k) {\n                float s"),
     ("depth_cap_one_short", "if (c.depth < D) {", "if (c.depth < D - 1) {"),
-    ("child_parented_to_grandparent", "Cand ch = {s, i, c.depth + 1, 0};", "Cand ch = {s, c.parent < 0 ? i : c.parent, c.depth + 1, 0};"),
+    ("child_parented_to_grandparent", "Cand ch = {s, i, c.depth + 1, rank_of[c.depth * K + k], k};",
+     "Cand ch = {s, c.parent < 0 ? i : c.parent, c.depth + 1, rank_of[c.depth * K + k], k};"),
+    ("rank_is_position", "Cand ch = {s, i, c.depth + 1, rank_of[c.depth * K + k], k};",
+     "Cand ch = {s, i, c.depth + 1, k, k};"),
+    ("ranking_ascending", "if (a->v != b->v) return a->v > b->v ? -1 : 1;",
+     "if (a->v != b->v) return a->v < b->v ? -1 : 1;"),
+    ("equal_values_later_index_first", "return a->k < b->k ? -1 : (a->k > b->k ? 1 : 0);",
+     "return a->k > b->k ? -1 : (a->k < b->k ? 1 : 0);"),
+    ("token_by_rank", "tokens[(c.depth - 1) * K + c.choice]", "tokens[(c.depth - 1) * K + c.rank]"),
 ]
 
 # Mistakes planted in the tree-accept / compaction oracle.
@@ -142,9 +150,12 @@ NEIGHBOUR_PINS = [
 TREE_PINS = [
     lambda: tree_pins.test_bruteforce_top_scores(3, 3, 20),
     lambda: tree_pins.test_bruteforce_top_scores(5, 3, 60),
+    lambda: tree_pins.test_bruteforce_top_scores_unsorted(3, 3, 20),
+    lambda: tree_pins.test_shuffled_choices_change_nothing(0),
+    tree_pins.test_equal_values_rank_by_index,
+    tree_pins.test_positive_log_prob_worked_example,
     tree_pins.test_tree_invariants,
     tree_pins.test_k1_is_a_chain_and_d1_is_a_star,
-    lambda: tree_pins.test_matches_offering_all_children(0),
     tree_pins.test_ties_go_to_the_earlier_parent_then_rank,
 ]
 

@@ -1,7 +1,13 @@
 """The best-first draft-tree builder on the GPU against its oracle (bit for bit:
 parents, depths, ranks and tokens are integers; scores are float32 sums taken in
 the same order), then end to end: trees built on the device feed the visibility
-builder and the attention step with no host round trip."""
+builder and the attention step with no host round trip.
+
+The kernel answers from its level pass when every log-probability is <= 0 and
+no scores tie, and from its one-node-per-step pass otherwise (ties, positive
+values, more candidates than the level pass holds); the cases below reach both:
+drafter log-probs in descending and in shuffled order, tie-heavy and positive
+inputs, and the largest staging table."""
 import numpy as np
 import pytest
 
@@ -58,6 +64,57 @@ def test_tree_matches_oracle(B, D, K, Q):
     rc, ref = oracle.build_tree(lp, Q, tok)
     assert rc == oracle.REF_OK
     assert_same_tree(gpu_tree(lp, Q, tok), ref, f"B{B} D{D} K{K} Q{Q}")
+
+
+def shuffled(lp, tok, seed):
+    rng = np.random.default_rng(seed)
+    perm = np.argsort(rng.random(lp.shape), axis=-1)
+    return (np.ascontiguousarray(np.take_along_axis(lp, perm, -1)),
+            np.ascontiguousarray(np.take_along_axis(tok, perm, -1)))
+
+
+@pytest.mark.parametrize("B,D,K,Q", [
+    (8, 12, 4, 128),      # the benchmarked trees
+    (3, 6, 8, 200),
+    (2, 1, 30, 31),       # star
+    (4, 9, 64, 256),      # most choices, largest tree
+    (70, 8, 3, 40),       # many batch rows
+])
+def test_tree_unsorted_matches_oracle(B, D, K, Q):
+    """Choices in no particular order: ranked by value inside the kernel.  With
+    token ids, and without them (the token is then the choice's index)."""
+    say(f"tree unsorted B{B} D{D} K{K} Q{Q}")
+    lp, tok = shuffled(*wl.drafter_topk(6300 + B + D + K + Q, B, D, K), seed=Q)
+    rc, ref = oracle.build_tree(lp, Q, tok)
+    assert rc == oracle.REF_OK
+    assert_same_tree(gpu_tree(lp, Q, tok), ref, f"unsorted B{B} D{D} K{K} Q{Q}")
+    rc, ref = oracle.build_tree(lp, Q)
+    assert_same_tree(gpu_tree(lp, Q), ref, f"unsorted, no tokens, B{B} D{D} K{K} Q{Q}")
+
+
+def test_tree_positive_log_probs():
+    """Values above 0 (a child can outscore its parent): the one-node-per-step pass."""
+    lp, tok = wl.drafter_topk(6400, 5, 10, 4)
+    lp = lp.copy()
+    lp[:, 3, :] += 3.0                     # depth 4's choices all positive
+    lp[1, 0, 2] = 0.5
+    lp = np.ascontiguousarray(lp, dtype=np.float32)
+    assert (lp > 0).any()
+    rc, ref = oracle.build_tree(lp, 100, tok)
+    assert rc == oracle.REF_OK
+    assert_same_tree(gpu_tree(lp, 100, tok), ref, "positive values")
+
+
+def test_tree_largest_staging_table():
+    """D = 256 depths x K = 64 choices at Q = 256: the rank-ordered tables take
+    80 KiB of LDS; shuffled and sorted choices."""
+    lp, tok = wl.drafter_topk(6500, 2, 256, 64)
+    rc, ref = oracle.build_tree(lp, 256, tok)
+    assert rc == oracle.REF_OK
+    assert_same_tree(gpu_tree(lp, 256, tok), ref, "largest table, sorted")
+    lp2, tok2 = shuffled(lp, tok, 6501)
+    rc, ref = oracle.build_tree(lp2, 256, tok2)
+    assert_same_tree(gpu_tree(lp2, 256, tok2), ref, "largest table, shuffled")
 
 
 def test_tree_ties_and_optional_outputs():

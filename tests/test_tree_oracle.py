@@ -1,16 +1,19 @@
 """Pins of the best-first draft-tree builder's oracle (CPU only).
 
-The oracle takes nodes off a binary heap.  These tests check it against what
-holds independently of that:
-- brute force: for log-probabilities sorted within each depth, a child never
-  scores above its parent or a better-ranked sibling, so the best-first tree of
-  Q nodes is the root plus the Q-1 highest-scoring nodes of the whole lattice of
-  choice paths (enumerated and sorted here), in score order;
+The oracle takes nodes off a binary heap into which every taken node pushes all
+K children.  These tests check it against what holds independently of that:
+- brute force: with log-probabilities <= 0 a child never scores above its
+  parent, and a better-ranked sibling never scores below a worse one, so the
+  best-first tree of Q nodes is the root plus the Q-1 highest-scoring nodes of
+  the whole lattice of choice paths (enumerated and sorted here), in score
+  order -- for choices given in descending order and for shuffled ones;
+- shuffling the K choices of a depth (with their token ids) changes nothing:
+  the ranking is by value, not by position;
 - the tree's own invariants, and the special cases that have a closed form:
-  K = 1 gives a chain, D = 1 a star in rank order;
-- ties go to the candidate whose parent was taken first, then the better rank
-  (the order of offering all K children at once), checked against a direct
-  eager implementation;
+  K = 1 gives a chain, D = 1 a star in rank order (equal values ranked by
+  index), and a worked example with a positive log-probability, where a
+  child outscores the nodes taken before it;
+- ties go to the candidate whose parent was taken first, then the better rank;
 - argument errors.
 """
 import itertools
@@ -30,13 +33,21 @@ def sorted_logp(rng, B, D, K, vocab=32, sigma=2.0):
     return np.take_along_axis(lp, order, -1).astype(np.float32), order.astype(np.int32)
 
 
-def paths(t, b, Q):
-    """Choice path (tuple of ranks) of every node of batch row b."""
+def paths(t, b, Q, key="rank"):
+    """Choice path (tuple of ranks, or of choice indices with key="token" when the
+    tree was built without token ids) of every node of batch row b."""
     out = []
     for i in range(Q):
         p = t["parent"][b, i]
-        out.append(() if p < 0 else out[p] + (int(t["rank"][b, i]),))
+        out.append(() if p < 0 else out[p] + (int(t[key][b, i]),))
     return out
+
+
+def shuffled(lp, tok, seed):
+    """The same choices in a random order within each (batch row, depth)."""
+    rng = np.random.default_rng(seed)
+    perm = np.argsort(rng.random(lp.shape), axis=-1)
+    return np.take_along_axis(lp, perm, -1), np.take_along_axis(tok, perm, -1)
 
 
 def lattice(lp, D, K):
@@ -66,6 +77,68 @@ def test_bruteforce_top_scores(D, K, Q):
         want = [()] + [nodes[i][0] for i in order]
         assert paths(t, b, Q) == want
         np.testing.assert_array_equal(t["score"][b], [0.0] + [scores[i] for i in order])
+
+
+@pytest.mark.parametrize("D,K,Q", [(3, 3, 20), (4, 2, 25), (2, 5, 31), (5, 3, 60)])
+def test_bruteforce_top_scores_unsorted(D, K, Q):
+    """Choices in a random order: the tree, read as paths of choice indices, is
+    still the root plus the Q-1 best lattice nodes, enumerated over the choices
+    in their given order."""
+    rng = np.random.default_rng(200 * D + K)
+    lp, tok = sorted_logp(rng, 4, D, K)
+    lp, _ = shuffled(lp, tok, 300 + D)
+    rc, t = oracle.build_tree(lp, Q)              # no token ids: token = choice index
+    assert rc == oracle.REF_OK
+    for b in range(4):
+        nodes = lattice(lp[b], D, K)
+        scores = np.array([s for _, s in nodes])
+        assert len(np.unique(scores)) == len(scores)
+        order = np.argsort(-scores, kind="stable")[: Q - 1]
+        assert paths(t, b, Q, key="token") == [()] + [nodes[i][0] for i in order]
+        np.testing.assert_array_equal(t["score"][b], [0.0] + [scores[i] for i in order])
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_shuffled_choices_change_nothing(seed):
+    """Permuting the K choices of every depth, together with their token ids,
+    leaves parents, depths, ranks, tokens and scores unchanged (values distinct)."""
+    rng = np.random.default_rng(40 + seed)
+    lp, tok = sorted_logp(rng, 5, 12, 4)
+    rc, want = oracle.build_tree(lp, 128, tok)
+    assert rc == oracle.REF_OK
+    lp2, tok2 = shuffled(lp, tok, 50 + seed)
+    assert not np.array_equal(lp2, lp)
+    rc, got = oracle.build_tree(lp2, 128, tok2)
+    assert rc == oracle.REF_OK
+    for k in ("parent", "depth", "rank", "token", "score"):
+        np.testing.assert_array_equal(got[k], want[k], err_msg=k)
+
+
+def test_equal_values_rank_by_index():
+    """A star (D = 1) is the choices in rank order; equal log-probabilities rank
+    by their index, so the root's children come out as choices 1, 2, 0, 3."""
+    lp = np.array([[[-1.0, -0.5, -0.5, -2.0]]], np.float32)
+    rc, t = oracle.build_tree(lp, 5)
+    assert rc == oracle.REF_OK
+    np.testing.assert_array_equal(t["parent"][0], [-1, 0, 0, 0, 0])
+    np.testing.assert_array_equal(t["token"][0], [-1, 1, 2, 0, 3])
+    np.testing.assert_array_equal(t["rank"][0], [-1, 0, 1, 2, 3])
+    np.testing.assert_array_equal(t["score"][0], [0.0, -0.5, -0.5, -1.0, -2.0])
+
+
+def test_positive_log_prob_worked_example():
+    """Best first is not the top-Q lattice set when a choice has a positive value:
+    depth 1 offers (-1, -2), depth 2 offers (+5, -1).  Taken in order: the root;
+    (-1) from the root; its child +5 scoring 4; then of the two candidates at -2
+    the one whose parent (the root) was taken first."""
+    lp = np.array([[[-1.0, -2.0], [5.0, -1.0]]], np.float32)
+    rc, t = oracle.build_tree(lp, 4)
+    assert rc == oracle.REF_OK
+    np.testing.assert_array_equal(t["parent"][0], [-1, 0, 1, 0])
+    np.testing.assert_array_equal(t["depth"][0], [0, 1, 2, 1])
+    np.testing.assert_array_equal(t["rank"][0], [-1, 0, 0, 1])
+    np.testing.assert_array_equal(t["token"][0], [-1, 0, 0, 1])
+    np.testing.assert_array_equal(t["score"][0], [0.0, -1.0, 4.0, -2.0])
 
 
 def test_tree_invariants():
@@ -107,9 +180,10 @@ def test_k1_is_a_chain_and_d1_is_a_star():
 
 
 def eager_tree(lp, Q):
-    """Best-first with every child offered at once (a sorted list scanned for its
-    best entry each step): the definition the one-at-a-time oracle must match."""
+    """Best-first with every child offered at once, a plain list scanned for its
+    best entry each step (ranks from Python's sort of each depth's choices)."""
     D, K = lp.shape
+    rank = [{k: r for r, k in enumerate(sorted(range(K), key=lambda k: (-lp[d, k], k)))} for d in range(D)]
     cand = [(np.float32(0.0), -1, 0, -1)]           # (score, parent, depth, rank)
     par, rk = [], []
     score = []
@@ -119,17 +193,18 @@ def eager_tree(lp, Q):
         i = len(par)
         par.append(p), rk.append(r), score.append(s)
         if d < D:
-            cand += [(np.float32(s + lp[d, k]), i, d + 1, k) for k in range(K)]
+            cand += [(np.float32(s + lp[d, k]), i, d + 1, rank[d][k]) for k in range(K)]
     return par, rk, score
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_matches_offering_all_children(seed):
     rng = np.random.default_rng(seed)
-    lp, _ = sorted_logp(rng, 3, 5, 4)
+    lp, tok = sorted_logp(rng, 3, 5, 4)
     lp[:, :, 2] = lp[:, :, 1]                       # ties between siblings
     lp[1] = np.round(lp[1])                         # many ties across branches
-    lp[1] = -np.sort(-lp[1], axis=-1)
+    lp[2] = np.round(lp[2] * 2) / 2
+    lp, _ = shuffled(lp, tok, 60 + seed)           # and in no particular order
     rc, t = oracle.build_tree(lp, 90)
     assert rc == oracle.REF_OK
     for b in range(3):

@@ -43,7 +43,7 @@ struct AttnArgs {
 
 // Everything the draft-tree builder needs (passed by value).
 struct TreeArgs {
-    const float* logp;       // [B][D][K], sorted descending within each [b][d]
+    const float* logp;       // [B][D][K], any order within each [b][d]
     const int32_t* tokens;   // [B][D][K] or null
     int32_t* parent;         // [B][Q]
     int32_t* depth;          // [B][Q] or null
