@@ -1,7 +1,10 @@
 """S2..S7 on the GPU against the CPU oracle, element by element.
 
-Bar: |gpu - oracle| <= 1e-4 + 1e-4 |oracle| for float32 caches and
-2e-2 + 2e-2 |oracle| for bf16 caches, on every output element and on lse.
+Bar (tests/parity.py), by the arithmetic that produced the output: fp32
+arithmetic (every cache type widened exactly) within 1e-4 + 1e-4 |oracle| on
+every element and on lse; the bf16 matrix-core kernel within 2e-2 relative L2
+on every query row, every element within 2e-2 of its row's rms plus 2e-2
+|oracle|, lse within 2e-2.
 Small and reduced workloads are compared in full; the full-size dense workloads
 run in the launch configuration the benchmark times and are compared on a
 seeded sample of rows (plus properties that hold for every row).
@@ -13,7 +16,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from parity import assert_close, assert_lse_close, oracle_rows, say
+from parity import BF16, F32, arithmetic, assert_close, assert_lse_close, oracle_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -36,8 +39,9 @@ def check_full(w, path=0, split_len=0, what=None, wg_order=0):
     r, out, lse = run(w, path, split_len, wg_order=wg_order)
     assert np.array_equal(r.bits(), bits)
     ref, rlse = oracle_rows(w, bits)
-    e = assert_close(out, ref, w.kv_dtype, what)
-    assert_lse_close(lse, rlse, w.kv_dtype, what)
+    ar = arithmetic(w.kv_dtype, r.plan()[1])
+    e = assert_close(out, ref, ar, what)
+    assert_lse_close(lse, rlse, ar, what)
     say(f"  {what}: plan={r.plan()} max abs err {e:.2e}")
     return r, out, lse
 
@@ -77,13 +81,9 @@ def test_dense_reduced_bf16(path):
     w = wl.make_workload("c5-small", 2005, B=3, H=64, Q=64, prefix=[0, 77, 700], tree="uniform",
                          kv_dtype=wl.BF16)
     r, out, lse = check_full(w, path=path)
-    if path != 0:
-        # the fp32-arithmetic paths on bf16 caches meet the fp32 bar as well
-        bits, _, _ = oracle.build_visibility(w.parent)
-        ref, _ = oracle_rows(w, bits)
-        assert_close(out, ref, 0, f"c5-small path {path} at the fp32 bar")
-    else:
-        assert r.plan()[1] == 2
+    # the VALU and fp32-MFMA paths widen the bf16 cache exactly: check_full held them
+    # to the fp32 bar; auto takes the bf16 matrix cores
+    assert (r.plan()[1] == 2) == (path == 0)
 
 
 def test_bf16_mfma_split_and_ragged():
@@ -277,7 +277,7 @@ def test_malformed_tree_still_runs():
 
 
 # ----------------------------------------------------------------------------- full sizes, sampled rows
-def _full_sampled(name, n_rows):
+def _full_sampled(name, n_rows, extra_rows=None):
     say(f"generate {name}")
     w = wl.config(name)
     bits, _, _ = oracle.build_visibility(w.parent)
@@ -291,11 +291,24 @@ def _full_sampled(name, n_rows):
     kvmax = float(np.abs({0: lambda a: a, 1: wl.bf16_bits_to_f32, 2: wl.fp8_bits_to_f32}[w.kv_dtype](head)).max())
     assert np.abs(out).max() <= 10 * kvmax
     rows = wl.sample_rows(w, n_rows)
+    if extra_rows is not None:
+        rows = np.unique(np.concatenate([rows, extra_rows(w)]))
     say(f"oracle {name} on {len(rows)} rows")
     ref, rlse = oracle_rows(w, bits, rows, chunk=4)
-    e = assert_close(out[rows], ref, w.kv_dtype, name)
-    assert_lse_close(lse[rows], rlse, w.kv_dtype, name)
+    ar = arithmetic(w.kv_dtype, r.plan()[1])
+    e = assert_close(out[rows], ref, ar, name)
+    assert_lse_close(lse[rows], rlse, ar, name)
     say(f"  {name}: max abs err {e:.2e} on {len(rows)} sampled rows")
+
+
+def _all_heads_of_some_nodes(w):
+    """Every head of nodes 0, 1, Q/2 and Q-1 of the batch rows with the longest and
+    the shortest prefix."""
+    rows = []
+    for b in (int(np.argmax(w.prefix)), int(np.argmin(w.prefix))):
+        for q in sorted({0, 1, w.Q // 2, w.Q - 1}):
+            rows.append((b * w.Q + q) * w.H + np.arange(w.H))
+    return np.concatenate(rows).astype(np.int64)
 
 
 @functools.lru_cache(maxsize=1)
@@ -343,7 +356,10 @@ def test_c4_decode_shape_row_half_full_sampled():
 
 
 def test_c5_full_sampled():
-    _full_sampled("c5", 32)
+    """c5 at full size in the benchmark's launch on the bf16 matrix cores: 256
+    seeded rows over all batch rows plus all 64 heads of four nodes of the longest
+    and the shortest batch row (768 rows), against the bf16-arithmetic bar."""
+    _full_sampled("c5", 256, extra_rows=_all_heads_of_some_nodes)
 
 
 # ----------------------------------------------------------------------------- graph capture
@@ -365,8 +381,9 @@ def test_step_replays_from_a_hip_graph(kv_dtype):
     bits, _, _ = oracle.build_visibility(w.parent)
     ref, rlse = oracle_rows(w, bits)
     out0, lse0 = r.results()
-    assert_close(out0, ref, kv_dtype, "graph eager")
-    assert_lse_close(lse0, rlse, kv_dtype, "graph eager")
+    ar = arithmetic(kv_dtype, r.plan()[1])
+    assert_close(out0, ref, ar, "graph eager")
+    assert_lse_close(lse0, rlse, ar, "graph eager")
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

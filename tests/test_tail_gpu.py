@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from parity import assert_close, assert_lse_close, oracle_rows, say
+from parity import F32, arithmetic, assert_close, assert_lse_close, oracle_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -71,9 +71,10 @@ def test_tail_mode_equals_full_attention(kv_dtype, split_len, want_lse, path):
     bits, _, _ = oracle.build_visibility(w.parent)
     ref, rlse = oracle_rows(w, bits)
     # the sparse route computes in fp32 on every cache dtype: the fp32 bar holds for it
-    e = assert_close(out, ref, kv_dtype if (path or split_len) else 0, "tail mode")
+    ar = arithmetic(kv_dtype, r.plan()[1]) if (path or split_len) else F32
+    e = assert_close(out, ref, ar, "tail mode")
     if want_lse:
-        assert_lse_close(lse, rlse, kv_dtype, "tail mode")
+        assert_lse_close(lse, rlse, ar, "tail mode")
     say(f"  max abs err {e:.2e}")
 
 
