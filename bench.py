@@ -134,6 +134,20 @@ def load_traffic(config_name, kernel_hash):
     return t.get("bytes_per_launch")
 
 
+def load_counters(config_name, kernel_hash):
+    """Matrix-pipe busy fraction per SIMD of the attention kernel from a committed
+    rocprofv3 counter summary (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE),
+    or None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"counters_attn_{config_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_hash:
+        return None
+    return t.get("mfma_busy_per_simd")
+
+
 # ----------------------------------------------------------------------------- CPU baseline (oracle)
 def time_tree_builder(dd, hip, stream, dev, B, Q, D=12, K=4, steps=20, warmup=3):
     """The draft-tree builder (ddtv_build_tree) on B trees of Q nodes from synthetic
@@ -231,12 +245,20 @@ def time_tail_mode(dd, hip, stream, r, steps=20, warmup=3):
             "dense_route_us_per_call": round(us_dense, 2), "calls": steps}
 
 
-def time_iteration(dd, hip, stream, r, V=32768, D=12, K=4, steps=10, warmup=2):
+def time_iteration(dd, hip, stream, r, V=32768, D=12, K=4, steps=10, warmup=2, grow=False):
     """One whole tree-verify iteration on the device at the benchmarked batch, tree
     size and cache: draft-tree builder -> visibility -> the tree's cache rows ->
     query preparation -> attention (S2..S7) -> value projection -> greedy
     acceptance with compaction.  Synthetic drafter top-K, projections, weights and
-    target logits; the resident cache; average iteration time from HIP events."""
+    target logits; the resident cache; average iteration time from HIP events.
+    The attention goes through the no-allocation entry point, so no workspace is
+    sized per plan.
+
+    grow=True: every iteration's prefixes are the last ones plus an accepted
+    length + 1 (accepted lengths drawn from a seeded sequence on the host, as a
+    decode loop that tracks the cache end would see them), so the batch rows'
+    cache offsets and the split plan are recomputed every iteration.  The caches
+    get room for the growth (the rows past the benchmarked cache hold zeros)."""
     import torch
     import workloads as wl
     w = r.w
@@ -253,39 +275,56 @@ def time_iteration(dd, hip, stream, r, V=32768, D=12, K=4, steps=10, warmup=2):
     q_rope = torch.empty((B, Q, H, 64), dtype=torch.float32, device=dev)
     v = torch.empty((B, Q, H, 128), dtype=torch.float32, device=dev)
     vis_buf = torch.empty(dd.ddtv_vis_bytes(B, Q), dtype=torch.uint8, device=dev)
-    prefix = np.ascontiguousarray(w.prefix, dtype=np.int32)
-    state = {}
+    n_iter = warmup + steps
+    prefixes = [np.ascontiguousarray(w.prefix, dtype=np.int32)]
+    if grow:
+        acc = np.random.default_rng(7700 + B + Q).integers(0, min(D, Q - 1) + 1, size=(n_iter, B))
+        for i in range(n_iter - 1):
+            prefixes.append((prefixes[-1] + acc[i] + 1).astype(np.int32))
+        extra = int((prefixes[-1].astype(np.int64) - prefixes[0]).sum())
+        ckv = torch.zeros((r.ckv.shape[0] + extra,) + tuple(r.ckv.shape[1:]), dtype=r.ckv.dtype, device=dev)
+        krope = torch.zeros((r.k_rope.shape[0] + extra,) + tuple(r.k_rope.shape[1:]), dtype=r.k_rope.dtype,
+                            device=dev)
+        ckv[: r.ckv.shape[0]].copy_(r.ckv)
+        krope[: r.k_rope.shape[0]].copy_(r.k_rope)
+    else:
+        prefixes *= n_iter
+        ckv, krope = r.ckv, r.k_rope
+    keep = []
 
-    def iteration():
+    def iteration(i):
         ok = dd.DDTV_OK
         assert dd.ddtv_build_tree(lp_d, Q, parent, tokens=tok_d, token=token, stream=stream) == ok
-        rc, vis = dd.ddtv_build_visibility(parent, prefix, B, Q, vis_buf, stream=stream)
+        rc, vis = dd.ddtv_build_visibility(parent, prefixes[i], B, Q, vis_buf, stream=stream)
         assert rc == ok
-        if "ws" not in state:
-            need = dd.ddtv_workspace_bytes(vis, H, w.kv_dtype)
-            state["ws"] = (torch.empty(max(need, 1), dtype=torch.uint8, device=dev), need)
-        ws, need = state["ws"]
-        assert dd.ddtv_append_kv(lat, k_pe, vis, r.ckv, r.k_rope, w.kv_dtype, nb.theta, stream=stream) == ok
+        assert dd.ddtv_append_kv(lat, k_pe, vis, ckv, krope, w.kv_dtype, nb.theta, stream=stream) == ok
         assert dd.ddtv_prepare_query(q, w_kc, vis, q_abs, q_rope, nb.theta, stream=stream) == ok
-        assert dd.ddtv_verify_attn(q_abs, q_rope, r.ckv, r.k_rope, w.kv_dtype, H, vis, w.scale, r.out, r.lse, ws,
-                                   need, stream=stream) == ok
+        # the split partials go to the library's scratch: no workspace to size per plan
+        assert dd.ddtv_verify_attn_noalloc(q_abs, q_rope, ckv, krope, w.kv_dtype, H, vis, w.scale, r.out, r.lse,
+                                           stream=stream) == ok
         assert dd.ddtv_value_proj(r.out, w_vc, v, stream=stream) == ok
-        assert dd.ddtv_tree_accept(logits, parent, token, vis, pred, path, out_tok, alen, ckv=r.ckv,
-                                   k_rope=r.k_rope, kv_dtype=w.kv_dtype, stream=stream) == ok
-        state["vis"] = vis   # keep the struct's borrowed arrays alive until the stream drains
-    for _ in range(warmup):
-        iteration()
+        assert dd.ddtv_tree_accept(logits, parent, token, vis, pred, path, out_tok, alen, ckv=ckv,
+                                   k_rope=krope, kv_dtype=w.kv_dtype, stream=stream) == ok
+        keep.append(vis)   # the struct's borrowed arrays stay alive until the stream drains
+    for i in range(warmup):
+        iteration(i)
     e0, e1 = hip.event(), hip.event()
     hip.record(e0, stream)
-    for _ in range(steps):
-        iteration()
+    t0 = time.perf_counter()
+    for i in range(warmup, n_iter):
+        iteration(i)
+    host_us = (time.perf_counter() - t0) * 1e6 / steps
     hip.record(e1, stream)
     us = hip.elapsed_ms(e0, e1) * 1e3 / steps
-    return {"workload": f"builder (top-{K} per depth, depth {D}) -> visibility -> cache append -> query prep "
-                        f"(d_nope 128) -> attention -> value projection (d_v 128) -> acceptance over {V} logits "
-                        "per node with compaction, on the benchmarked batch and cache",
-            "us_per_iteration": round(us, 2), "tree_tokens_per_s": round(B * Q / (us * 1e-6), 1),
-            "iterations": steps}
+    res = {"workload": f"builder (top-{K} per depth, depth {D}) -> visibility -> cache append -> query prep "
+                       f"(d_nope 128) -> attention -> value projection (d_v 128) -> acceptance over {V} logits "
+                       "per node with compaction, on the benchmarked batch and cache",
+           "us_per_iteration": round(us, 2), "tree_tokens_per_s": round(B * Q / (us * 1e-6), 1),
+           "host_enqueue_us_per_iteration": round(host_us, 2), "iterations": steps}
+    if grow:
+        res["workload"] += "; prefixes grow by a seeded accepted length + 1 every iteration (plans recomputed)"
+        res["prefix_growth"] = int((prefixes[-1].astype(np.int64) - prefixes[0]).sum())
+    return res
 
 
 def time_fp8_cache(dd, hip, stream, r, flops, steps=10, warmup=2):
@@ -382,14 +421,30 @@ def time_neighbour(dd, hip, stream, r, d_nope=128, d_v=128, steps=20, warmup=3):
     return res
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, budget_s=15.0, max_rows=4096):
     """The oracle (single-threaded fp64 C) on a seeded sample of query rows of the
-    same workload, for about budget_s seconds.  Reported as tree-query tokens/s
-    (rows/s divided by H: one token is one tree node across all heads)."""
+    same workload, for about budget_s seconds, pinned to one host core.  Reported
+    as tree-query tokens/s (rows/s divided by H: one token is one tree node across
+    all heads)."""
     import oracle
     import workloads as wl
     bits, _, _ = oracle.build_visibility(w.parent)
     rows = wl.sample_rows(w, max_rows, seed=11)
+    pinned = None
+    if hasattr(os, "sched_setaffinity"):
+        pinned = min(os.sched_getaffinity(0))
+        os.sched_setaffinity(0, {pinned})
     done = 0
     t0 = time.perf_counter()
     while done < len(rows) and time.perf_counter() - t0 < budget_s:
@@ -399,9 +454,67 @@ def cpu_baseline(w, budget_s=15.0, max_rows=4096):
         done += k
     dt = time.perf_counter() - t0
     return {"value": round(done / dt / w.H, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(), "pinned_cpu": pinned,
             "sample": f"{done} seeded (b,q,h) query rows of the same workload (all batch rows), "
-                      f"{dt:.1f} s on 1 host core ({platform.processor() or platform.machine()}); "
-                      f"tokens/s = rows/s / H"}
+                      f"{dt:.1f} s on 1 host core pinned by affinity; tokens/s = rows/s / H"}
+
+
+def measure(dd, hip, stream, w, K, warmup, path=0, split_len=0, wg_order=0, dev=None, traffic_name=None):
+    """Time K verify steps (S1..S7) of workload w after `warmup` untimed ones: the
+    step from events around all K, the attention kernel from events the library
+    records around it on the same stream.  Returns the run and a result dict."""
+    import workloads as wl
+    from tree_masked_mla_amd.runner import DeviceRun
+    r = DeviceRun(w, device=dev, path=path, split_len=split_len, want_lse=True, wg_order=wg_order)
+    rc, ppath, psplit, pn, pwgs, porder = r.plan()
+    log(f"{w.name}: plan path={ppath} split_len={psplit} n_split={pn} workgroups={pwgs} wg_order={porder}")
+    ev_attn = [(hip.event(), hip.event()) for _ in range(K)]
+    ev0, ev1 = hip.event(), hip.event()
+    for _ in range(warmup):
+        r.step(stream)
+    import torch
+    torch.cuda.synchronize()
+    t_host0 = time.perf_counter()
+    hip.record(ev0, stream)
+    for k in range(K):
+        r.step(stream, dd.make_opts(path, split_len, ev_attn[k][0], ev_attn[k][1], wg_order))
+    hip.record(ev1, stream)
+    torch.cuda.synchronize()
+    t_host1 = time.perf_counter()
+    ms_step = hip.elapsed_ms(ev0, ev1) / K
+    attn_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in ev_attn]))
+    nbytes, flops, vis_pairs = algorithmic(w)
+    bf16_mma = ppath == dd.DDTV_PATH_MFMA and w.kv_dtype == wl.BF16
+    valu = ppath == dd.DDTV_PATH_VALU
+    peak_key = "bf16-mfma" if bf16_mma else ("f32-valu" if valu else "f32-mfma")
+    kernel = "attn_mfma_bf16_kernel" if bf16_mma else ("attn_valu_kernel" if valu else "attn_mfma_kernel")
+    khash = kernel_source_hash(kernel)
+    roof = roofline_bound(valu, flops, nbytes, attn_ms, PEAK_TFLOPS[peak_key])
+    res = {
+        "ms_per_step": ms_step, "attn_ms": attn_ms, "host_ms_per_step": (t_host1 - t_host0) * 1e3 / K,
+        "tokens_per_s": w.B * w.Q / (ms_step / 1e3), "hbm_gbps": nbytes / (ms_step / 1e3) / 1e9,
+        "dtype": "bf16" if bf16_mma else "f32", "kernel": kernel, "kernel_source_hash": khash,
+        "flops": flops, "nbytes": nbytes, "vis_pairs": vis_pairs, "roofline": roof,
+        "traffic": load_traffic(traffic_name, khash) if traffic_name else None,
+        "mfma_busy": load_counters(traffic_name, khash) if traffic_name else None,
+        "plan": {"path": ppath, "split_len": psplit, "n_split": pn, "workgroups": pwgs,
+                 "wg_order": {1: "xcd-local", 2: "spread"}.get(porder, porder)},
+    }
+    return r, res
+
+
+def config_entry(name, w, desc, res, steps):
+    """One entry of the line's `configs` object."""
+    roof = dict(res["roofline"])
+    roof["traffic"] = res["traffic"]
+    return {"workload": f"{name}: {desc}", "dtype": res["dtype"],
+            "arithmetic": ("bf16 MFMA, fp32 accumulation: query and probabilities rounded to bf16"
+                           if res["dtype"] == "bf16" else "fp32 (cache values widened exactly)"),
+            "kernel": res["kernel"], "kernel_us": round(res["attn_ms"] * 1e3, 2),
+            "step_us": round(res["ms_per_step"] * 1e3, 2), "tokens_per_s": round(res["tokens_per_s"], 1),
+            "hbm_gbps": round(res["hbm_gbps"], 2), "roofline": roof, "mfma_busy": res["mfma_busy"],
+            "kernel_source_hash": res["kernel_source_hash"], "flops_per_launch": res["flops"],
+            "algorithmic_bytes_per_step": res["nbytes"], "plan": res["plan"], "steps": steps}
 
 
 # ----------------------------------------------------------------------------- main
@@ -418,6 +531,8 @@ def main():
                     help="override the workload's tree size (probe runs, e.g. q_len 1 = decode); "
                          "not the benchmarked configuration")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--no-configs", dest="configs", action="store_false",
+                    help="skip the other workloads (c3, c5, the q_len-1 probe) after the c4 headline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="instead of the bench, run N launches of a plain copy of the cache bytes "
@@ -455,44 +570,17 @@ def main():
                           "launches": args.copy_calibration}))
         return
 
-    r = DeviceRun(w, device=dev, path=args.path, split_len=args.split_len, want_lse=True, wg_order=args.wg_order)
-    rc, path, split_len, n_split, wgs, wg_order = r.plan()
-    log(f"plan: path={path} split_len={split_len} n_split={n_split} workgroups={wgs} wg_order={wg_order}")
     hip = Hip()
     stream = torch.cuda.current_stream(dev).cuda_stream
     K = args.steps
-    ev_attn = [(hip.event(), hip.event()) for _ in range(K)]
-    ev_step0, ev_step1 = hip.event(), hip.event()
-
-    for _ in range(args.warmup):
-        r.step(stream)
-    torch.cuda.synchronize()
-
-    t_host0 = time.perf_counter()
-    hip.record(ev_step0, stream)
-    for k in range(K):
-        opts = dd.make_opts(args.path, args.split_len, ev_attn[k][0], ev_attn[k][1], args.wg_order)
-        r.step(stream, opts)
-    hip.record(ev_step1, stream)
-    torch.cuda.synchronize()
-    t_host1 = time.perf_counter()
-
-    total_ms = hip.elapsed_ms(ev_step0, ev_step1)
-    attn_ms = [hip.elapsed_ms(a, b) for a, b in ev_attn]
-    ms_step = total_ms / K
-    attn_avg_ms = float(np.mean(attn_ms))
-
-    nbytes, flops, vis_pairs = algorithmic(w)
+    traffic_name = None if args.q_len else args.config
+    r, res = measure(dd, hip, stream, w, K, args.warmup, args.path, args.split_len, args.wg_order, dev,
+                     traffic_name)
+    ms_step, attn_avg_ms = res["ms_per_step"], res["attn_ms"]
     tokens = w.B * w.Q
     value = tokens / (ms_step / 1e3)
-    hbm_gbps = nbytes / (ms_step / 1e3) / 1e9
-    bf16_mma = path == dd.DDTV_PATH_MFMA and w.kv_dtype == wl.BF16
-    peak_key = "bf16-mfma" if bf16_mma else ("f32-valu" if path == dd.DDTV_PATH_VALU else "f32-mfma")
-    achieved_tflops = flops / (attn_avg_ms / 1e3) / 1e12
-    kernel = ("attn_mfma_bf16_kernel" if bf16_mma else
-              "attn_valu_kernel" if path == dd.DDTV_PATH_VALU else "attn_mfma_kernel")
-    khash = kernel_source_hash(kernel)
-    traffic = None if args.q_len else load_traffic(args.config, khash)
+    hbm_gbps = res["hbm_gbps"]
+    plan = res["plan"]
 
     out = {
         "metric": METRIC,
@@ -505,34 +593,50 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if bf16_mma else "f32",
+        "dtype": res["dtype"],
         "data": "synthetic",
         "config": {"workload": f"{args.config}: {desc}", "B": w.B, "H": w.H,
                    "q_len": w.Q, "prefix": "ragged" if args.config == "c5" else int(w.prefix[0]),
-                   "total_kv_rows": w.total_kv, "scale": w.scale, "path": path, "split_len": split_len,
-                   "n_split": n_split, "workgroups": wgs,
-                   "wg_order": {1: "xcd-local", 2: "spread"}.get(wg_order, wg_order)},
+                   "total_kv_rows": w.total_kv, "scale": w.scale, "path": plan["path"],
+                   "split_len": plan["split_len"], "n_split": plan["n_split"], "workgroups": plan["workgroups"],
+                   "wg_order": plan["wg_order"]},
         "hbm_gbps": round(hbm_gbps, 2),
         "hbm_pct_of_peak": round(100.0 * hbm_gbps / HBM_PEAK_GBPS, 3),
         "attn_kernel_us": round(attn_avg_ms * 1e3, 2),
         "step_us": round(ms_step * 1e3, 2),
-        "host_wall_ms_per_step": round((t_host1 - t_host0) * 1e3 / K, 4),
+        "host_wall_ms_per_step": round(res["host_ms_per_step"], 4),
         "roofline": {
-            **roofline_bound(path == dd.DDTV_PATH_VALU, flops, nbytes, attn_avg_ms, PEAK_TFLOPS[peak_key]),
-            "traffic": traffic,
-            "kernel": kernel,
-            "flops_per_launch": flops,
-            "algorithmic_bytes_per_step": nbytes,
-            "visible_pairs": vis_pairs,
-            "kernel_source_hash": khash,
+            **res["roofline"],
+            "traffic": res["traffic"],
+            "mfma_busy": res["mfma_busy"],
+            "kernel": res["kernel"],
+            "flops_per_launch": res["flops"],
+            "algorithmic_bytes_per_step": res["nbytes"],
+            "visible_pairs": res["vis_pairs"],
+            "kernel_source_hash": res["kernel_source_hash"],
         },
     }
     out["tree_build"] = time_tree_builder(dd, hip, stream, dev, w.B, w.Q)
     out["tail_mode"] = time_tail_mode(dd, hip, stream, r)
     out["tree_accept"] = time_tree_accept(dd, hip, stream, r)
     out["neighbour"] = time_neighbour(dd, hip, stream, r)
-    out["fp8_cache"] = time_fp8_cache(dd, hip, stream, r, flops)
+    out["fp8_cache"] = time_fp8_cache(dd, hip, stream, r, res["flops"])
     out["iteration"] = time_iteration(dd, hip, stream, r)
+    out["iteration_growing_prefix"] = time_iteration(dd, hip, stream, r, grow=True)
+    if args.configs and args.config == "c4" and not args.q_len:
+        # the other workloads, each in its own timed region (the headline above stays c4)
+        out["configs"] = {}
+        del r
+        torch.cuda.empty_cache()
+        for name, q_len, steps in (("c3", 0, max(K, 50)), ("c4_q_len_1", 1, K), ("c5", 0, K)):
+            base = "c4" if q_len else name
+            d = wl.DESCRIPTIONS[base] + (f" [decode probe: q_len {q_len}]" if q_len else "")
+            log(f"generating {name}: {d}")
+            wc = wl.config(base, Q=q_len) if q_len else wl.config(base)
+            rc_, res_c = measure(dd, hip, stream, wc, steps, args.warmup, dev=dev, traffic_name=name)
+            out["configs"][name] = config_entry(name, wc, d, res_c, steps)
+            del rc_
+            torch.cuda.empty_cache()
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(w, budget_s=args.cpu_budget)

@@ -436,3 +436,54 @@ def test_noalloc_host_errors(lib):
     assert call(opts=dd.make_opts(split_len=32)) == dd.DDTV_EWORKSPACE
     need = dd.ddtv_workspace_bytes(vis, 16, 0, dd.make_opts(split_len=32))
     assert need > dd.NOALLOC_SCRATCH_BYTES
+
+
+def workload_vis(name, q_len=None):
+    """A visibility struct with the geometry of a named workload (fake device
+    pointers: planning reads only the host-side fields)."""
+    import workloads as wl
+    parent, pre = wl.config_trees(name)
+    B, Q = parent.shape
+    if q_len is not None:
+        Q = q_len
+    H = {"c1": 8, "c2": 8, "c3": 16, "c4": 16, "c5": 64}[name]
+    return fake_vis(B, Q, tuple(int(x) for x in pre)), H
+
+
+@pytest.mark.parametrize("name,q_len,dtype,want", [
+    ("c3", None, 0, (2, 288, 15, 240, dd.DDTV_ORDER_XCD_LOCAL)),
+    ("c4", None, 0, (2, 32896, 1, 256, dd.DDTV_ORDER_XCD_LOCAL)),
+    ("c4", 1, 0, (2, 1056, 32, 256, dd.DDTV_ORDER_XCD_LOCAL)),
+    ("c5", None, 1, (2, None, 1, 2048, dd.DDTV_ORDER_SPREAD)),
+])
+def test_plans_of_the_benchmarked_workloads(lib, name, q_len, dtype, want):
+    """The split plans the measurements were taken with: c3 in 15 splits on 240
+    workgroups, c4 unsplit, c4 sizes at q_len 1 in 32 splits (row-half mode),
+    c5 unsplit in the spread order."""
+    vis, H = workload_vis(name, q_len)
+    rc, path, split_len, n_split, wgs, order = dd.ddtv_plan_info(vis, H, dtype)
+    assert rc == dd.DDTV_OK
+    got = (path, split_len, n_split, wgs, order)
+    for g, w in zip(got, want):
+        assert w is None or g == w, (name, got, want)
+
+
+@pytest.mark.parametrize("name,q_len,dtype", [("c5", None, 1), ("c4", 1, 0), ("c3", None, 0), ("c4", None, 0)])
+def test_uncached_planning_is_cheap(lib, name, q_len, dtype):
+    """A verify loop whose prefixes grow every step misses the plan cache each
+    call; planning must stay far below the GPU step it plans.  Median of 25
+    calls, each on prefixes one position longer than the last."""
+    import statistics
+    import time
+    vis0, H = workload_vis(name, q_len)
+    pre = np.ctypeslib.as_array(ctypes.cast(vis0.vis.prefix_host, ctypes.POINTER(ctypes.c_int32)), (vis0.vis.B,))
+    ts = []
+    for i in range(25):
+        vis = fake_vis(vis0.vis.B, vis0.vis.Q, tuple(int(x) + i + 1 for x in pre))
+        t0 = time.perf_counter()
+        rc = dd.ddtv_plan_info(vis, H, dtype)[0]
+        ts.append(time.perf_counter() - t0)
+        assert rc == dd.DDTV_OK
+    med = statistics.median(ts)
+    print(f"{name} q_len {q_len or vis0.vis.Q}: uncached plan {med * 1e6:.1f} us")
+    assert med < 200e-6, f"{name}: uncached planning took {med * 1e6:.0f} us"

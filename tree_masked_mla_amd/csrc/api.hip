@@ -71,6 +71,7 @@ bool grid_fits(int64_t workgroups, int threads) {
     return workgroups >= 0 && workgroups <= (int64_t)UINT32_MAX / threads;
 }
 
+constexpr int kMaxCusPerXcd = 64;              // planner's per-XCD CU table (MI355X: 32)
 constexpr int32_t kMaxProjHeads = 1024;          // heads per projection call (grid z)
 constexpr int64_t kMaxProjRows = (int64_t)1 << 28; // tokens per projection call: (rows / 64) x 512 threads < 2^32
 
@@ -104,44 +105,146 @@ struct Plan {
     size_t ws_part_o = 0, ws_part_ml = 0, ws_bytes = 0;
 };
 
+// One XCD under in-order dispatch: its CUs' free times, kept sorted ascending;
+// work items start in order on whichever CU frees first.  Consecutive items of
+// equal cost are gathered into one run before they are placed.
+struct XcdSchedule {
+    double t[kMaxCusPerXcd];
+    double tmp[kMaxCusPerXcd];
+    int P;
+    double pend_c;
+    int64_t pend_k;
+    void reset(int cus) {
+        P = cus;
+        for (int i = 0; i < P; ++i) t[i] = 0.0;
+        pend_k = 0;
+        pend_c = 0.0;
+    }
+    void add(double c, int64_t k) {
+        if (k <= 0) return;
+        if (pend_k > 0 && c == pend_c) {
+            pend_k += k;
+            return;
+        }
+        flush();
+        pend_c = c;
+        pend_k = k;
+    }
+    // a run of k items of cost c: each full round adds c to every CU, the
+    // remaining r items go to the r CUs that free first
+    void flush() {
+        if (pend_k == 0) return;
+        const double c = pend_c;
+        const int64_t full = pend_k / P;
+        const int r = (int)(pend_k % P);
+        pend_k = 0;
+        if (full)
+            for (int i = 0; i < P; ++i) t[i] += (double)full * c;
+        if (r == 0) return;
+        int i = 0, j = r, o = 0;   // merge t[0..r) + c with t[r..P)
+        while (i < r && j < P) tmp[o++] = (t[i] + c <= t[j]) ? t[i++] + c : t[j++];
+        while (i < r) tmp[o++] = t[i++] + c;
+        while (j < P) tmp[o++] = t[j++];
+        for (int q = 0; q < P; ++q) t[q] = tmp[q];
+    }
+    double makespan() {
+        flush();
+        return t[P - 1];
+    }
+};
+
+constexpr double kExitCost = 0.02;   // a work item past its row's last split: starts and exits
+
+// Total work of the grid spread evenly over all CUs, plus the merge pass: a
+// lower bound on the makespan, and one that grows with the split count (each
+// split adds its set-up and merge traffic).
+double fluid_bound(const std::vector<int>& kv, int n_rt, int L, int cus, double setup_tiles,
+                   double merge_tiles_per_partial_row_split, int64_t R, int parts_per_split) {
+    int n_split = 1;
+    for (int k : kv) n_split = std::max(n_split, (k + L - 1) / L);
+    const int full_tiles = (L + kTile - 1) / kTile;
+    double work = 0.0, merge = 0.0;
+    for (int k : kv) {
+        const int nb = (k + L - 1) / L;
+        const int last = k - (nb - 1) * L;
+        work += (double)n_rt * ((double)(nb - 1) * (setup_tiles + full_tiles) + setup_tiles +
+                                (double)((last + kTile - 1) / kTile) + (double)(n_split - nb) * kExitCost);
+        if (nb * parts_per_split > 1) merge += merge_tiles_per_partial_row_split * (double)(nb * parts_per_split) * (double)R;
+    }
+    return work / cus + merge;
+}
+
 // Estimated makespan (in tile-times) of the main kernel's grid plus the merge
 // pass.  The grid holds B x n_split x n_rt work items (batch row slowest, query
-// tile fastest; items past a short row's last split exit at once).  The
+// tile fastest); items past a short row's last split exit at once.  The
 // dispatcher deals workgroup i to XCD i % 8, and each XCD starts its workgroups
 // in order on whichever of its CUs frees first, one workgroup per CU at a time
 // (every attention kernel uses most of a CU's LDS).  Workgroup i runs work item
-// i (spread) or xcd_remap(i) (XCD-local).
+// i (spread) or xcd_remap(i) (XCD-local: each XCD a contiguous block).  The n_rt
+// query tiles of one (row, split) cost the same, so each XCD's list is
+// simulated run by run.  `bound`: give up (returning at least bound) once the
+// total work alone shows the plan cannot beat it.
 double estimate(const std::vector<int>& kv, int n_rt, int L, int cus, double setup_tiles,
-                double merge_tiles_per_partial_row_split, int64_t R, bool spread) {
-    typedef std::priority_queue<double, std::vector<double>, std::greater<double>> MinHeap;
-    const int per_xcd = std::max(1, cus / kXcds);
-    std::vector<MinHeap> free_at(kXcds);
-    for (auto& h : free_at)
-        for (int i = 0; i < per_xcd; ++i) h.push(0.0);
+                double merge_tiles_per_partial_row_split, int64_t R, int parts_per_split, bool spread,
+                double bound = 1e300) {
+    const int per_xcd = std::max(1, std::min(kMaxCusPerXcd, cus / kXcds));
     int n_split = 1;
     for (int k : kv) n_split = std::max(n_split, (k + L - 1) / L);
     const int64_t G = (int64_t)kv.size() * n_split * n_rt;
-    double makespan = 0.0, merge = 0.0;
+    double merge = 0.0;   // each partial row is written, then read by the merge pass
     for (int k : kv) {
-        const int nb = (k + L - 1) / L;
-        if (nb > 1) merge += merge_tiles_per_partial_row_split * (double)nb * (double)R;
+        const int parts = (k + L - 1) / L * parts_per_split;
+        if (parts > 1) merge += merge_tiles_per_partial_row_split * (double)parts * (double)R;
     }
-    if (G > ((int64_t)1 << 22)) {   // too many to simulate: thousands per CU even out
-        double work = 0.0;
-        for (int k : kv) work += (double)n_rt * ((k + kTile - 1) / kTile + setup_tiles * ((k + L - 1) / L));
-        return work / cus + merge;
-    }
-    for (int64_t i = 0; i < G; ++i) {
-        const int64_t w = spread ? i : xcd_remap(i, G);
-        const int b = (int)(w / ((int64_t)n_rt * n_split));
-        const int s = (int)((w / n_rt) % n_split);
+    auto cost = [&](int b, int s) {
         const int len = std::min(L, kv[b] - s * L);
-        const double cost = len > 0 ? setup_tiles + (len + kTile - 1) / kTile : 0.02;
-        MinHeap& h = free_at[i % kXcds];
-        const double t = h.top() + cost;
-        h.pop();
-        h.push(t);
-        makespan = std::max(makespan, t);
+        return len > 0 ? setup_tiles + (double)((len + kTile - 1) / kTile) : kExitCost;
+    };
+    const double fluid =
+        fluid_bound(kv, n_rt, L, cus, setup_tiles, merge_tiles_per_partial_row_split, R, parts_per_split);
+    if (fluid >= bound) return fluid;
+    if (G <= (int64_t)per_xcd * kXcds) {   // no XCD gets more items than CUs: all start at once
+        int longest = 0;
+        for (int k : kv) longest = std::max(longest, std::min(L, k));
+        return setup_tiles + (double)((longest + kTile - 1) / kTile) + merge;
+    }
+    if ((int64_t)kv.size() * n_split * kXcds > ((int64_t)1 << 20)) return fluid;   // thousands per CU even out
+    XcdSchedule X;
+    double makespan = 0.0;
+    if (spread) {
+        // XCD x takes the items i of each (row, split) with i % 8 == x; with n_rt a
+        // multiple of 8 every XCD gets the same list, so one stands for all
+        const int base = n_rt / kXcds, extra = n_rt % kXcds;
+        const int xcds = extra == 0 ? 1 : kXcds;
+        for (int x = 0; x < xcds; ++x) {
+            X.reset(per_xcd);
+            if (base == 0) {   // fewer than 8 query tiles per (row, split): visit this XCD's items only
+                for (int64_t i = x; i < G; i += kXcds) {
+                    const int64_t g = i / n_rt;
+                    X.add(cost((int)(g / n_split), (int)(g % n_split)), 1);
+                }
+            } else {
+                for (int b = 0; b < (int)kv.size(); ++b)
+                    for (int s = 0; s < n_split; ++s) {
+                        const int64_t g0 = ((int64_t)b * n_split + s) * n_rt;
+                        X.add(cost(b, s), base + ((((x - g0) % kXcds) + kXcds) % kXcds < extra ? 1 : 0));
+                    }
+            }
+            makespan = std::max(makespan, X.makespan());
+        }
+    } else {
+        const int64_t q = G / kXcds, r = G % kXcds;
+        for (int x = 0; x < kXcds; ++x) {
+            const int64_t lo = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+            const int64_t hi = lo + (x < r ? q + 1 : q);
+            if (hi <= lo) continue;
+            X.reset(per_xcd);
+            for (int64_t g = lo / n_rt; g * n_rt < hi; ++g) {   // (row, split) runs overlapping the block
+                const int64_t a0 = std::max(lo, g * n_rt), a1 = std::min(hi, (g + 1) * n_rt);
+                X.add(cost((int)(g / n_split), (int)(g % n_split)), a1 - a0);
+            }
+            makespan = std::max(makespan, X.makespan());
+        }
     }
     return makespan + merge;
 }
@@ -149,10 +252,10 @@ double estimate(const std::vector<int>& kv, int n_rt, int L, int cus, double set
 ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const ddtv_opts* opts,
                                size_t ws_cap, Plan* p);
 
-// Plans are pure functions of the shapes, the options, the device's CU count and
-// the per-row cache lengths; a verify loop re-plans the same shapes every step, so
-// the last few plans are kept (the split search simulates a schedule and is too
-// slow to repeat per call).
+// Plans are pure functions of the shapes, the options, the device's CU count, the
+// workspace limit and the per-row cache lengths; a verify loop over a fixed cache
+// re-plans the same shapes every step, so the last few plans are kept (a search
+// costs a few to a few tens of microseconds, a cached plan about two).
 struct PlanKey {
     int32_t B, Q, W, max_kv, H, dtype, path, split, order, has_order, cus;
     int64_t total_kv;
@@ -284,22 +387,24 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     // cache tile find it in its XCD's L2, so the spread order has to be clearly
     // shorter to be chosen (it is when batch rows differ in length: XCD-local
     // then gives each XCD whole rows).
-    auto cost_at = [&](int L, int* order) {
+    const int hm = p->halves ? 2 : 1;   // partials per split (row-half mode: one per half, always merged)
+    auto cost_at = [&](int L, int* order, double bound) {
         if (order_req != DDTV_ORDER_AUTO) {
             *order = order_req;
             return order_req == DDTV_ORDER_SPREAD
-                       ? estimate(kv_sorted, p->n_rt, L, cus, setup, merge_per_row_split, R, true)
-                       : estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, false);
+                       ? estimate(kv_sorted, p->n_rt, L, cus, setup, merge_per_row_split, R, hm, true, bound)
+                       : estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, hm, false, bound);
         }
-        const double local = estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, false);
-        const double spread = estimate(kv_sorted, p->n_rt, L, cus, setup, merge_per_row_split, R, true);
+        const double local = estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, hm, false, bound);
+        const double spread = estimate(kv_sorted, p->n_rt, L, cus, setup, merge_per_row_split, R, hm, true,
+                                       std::min(bound, local * 0.98));
         *order = spread < local * 0.98 ? DDTV_ORDER_SPREAD : DDTV_ORDER_XCD_LOCAL;
         return std::min(local, spread);
     };
 
     if (split_req > 0) {
         p->split_len = split_req;
-        cost_at(split_req, &p->order);
+        cost_at(split_req, &p->order, 1e300);
     } else {
         double best = 1e300;
         int bestL = single, bestOrder = DDTV_ORDER_XCD_LOCAL;
@@ -307,7 +412,8 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
         // Candidates: the longest row cut into S equal tile-aligned pieces, S = 1, 2, ...
         // (stop once the grid is far beyond the device or pieces get short).
         int prevL = 0, worse = 0;
-        for (int S = 1;; ++S) {
+        // (every S below 32, then steps of S / 32: the split lengths grow dense)
+        for (int S = 1;; S += S < 32 ? 1 : S / 32) {
             const int L = (int)round_up((size_t)((max_kv + S - 1) / S), kSplitQuantum);
             if (L < 4 * kTile && S > 1) break;
             if (L == prevL) continue;
@@ -317,8 +423,10 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
             if (wgs > wg_cap && S > 1) break;
             const int parts_L = ((max_kv + L - 1) / L) * (p->halves ? 2 : 1);
             if (S > 1 && partial_bytes(vis->B, R, parts_L) > ws_cap) break;   // more splits only need more
+            if (S > 1 && fluid_bound(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, hm) >= best * 0.98)
+                break;   // its lower bound cannot beat the best by 2 %, nor can more splits'
             int order = DDTV_ORDER_XCD_LOCAL;
-            const double e = cost_at(L, &order);
+            const double e = cost_at(L, &order, best * 0.98);   // a plan must beat the best by 2 %
             if (e < best * 0.98) {   // prefer fewer splits unless clearly better
                 best = e;
                 bestL = L;
