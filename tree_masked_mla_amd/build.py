@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libddtv.so")
 
-SOURCES = ["api.hip", "visibility.hip", "attn_valu.hip", "attn_mfma.hip", "attn_mfma_bf16.hip", "attn_mfma_bf16w.hip", "merge.hip",
+SOURCES = ["api.hip", "visibility.hip", "attn_valu.hip", "attn_mfma.hip", "attn_mfma_bf16.hip", "merge.hip",
            "tree_build.hip", "tree_accept.hip", "tail.hip", "neighbour.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -249,9 +249,6 @@ double estimate(const std::vector<int>& kv, int n_rt, int L, int cus, double set
     return makespan + merge;
 }
 
-// bf16 matrix-core kernel: 32 query rows per wave (true) or 16 (false).
-constexpr bool kBf16Wide = false;
-
 ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dtype, const ddtv_opts* opts,
                                size_t ws_cap, Plan* p);
 
@@ -359,7 +356,7 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     // mode: two wave pairs share each 16-row group and split every cache tile.
     p->halves = p->path != DDTV_PATH_VALU && !p->bf16_mma && R <= 32;
     p->rows_per_wg = p->path == DDTV_PATH_VALU ? kValuRows
-                     : p->bf16_mma             ? (kBf16Wide ? bf16w_rows_per_workgroup() : bf16_rows_per_workgroup())
+                     : p->bf16_mma             ? bf16_rows_per_workgroup()
                      : p->halves               ? 32
                                                : mfma_rows_per_workgroup(kv_dtype);
     if (R > (int64_t)INT32_MAX / 2) return DDTV_EUNSUPPORTED;
@@ -527,8 +524,7 @@ ddtv_status launch_verify(const Plan& p, const float* q_abs, const float* q_rope
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 
     if (opts && opts->attn_begin && hipEventRecord(opts->attn_begin, stream) != hipSuccess) return DDTV_EDEVICE;
-    hipError_t e = p.bf16_mma ? (kBf16Wide ? launch_attn_mfma_bf16w(a, p.grid, stream)
-                                           : launch_attn_mfma_bf16(a, p.grid, stream))
+    hipError_t e = p.bf16_mma ? launch_attn_mfma_bf16(a, p.grid, stream)
                    : (p.path == DDTV_PATH_VALU) ? launch_attn_valu(a, kv_dtype, p.grid, stream)
                                                 : launch_attn_mfma(a, kv_dtype, p.grid, stream);
     if (e != hipSuccess) return DDTV_EDEVICE;

@@ -85,8 +85,6 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int kv_dtype, int64_t grid, hipSt
 int mfma_rows_per_workgroup(int kv_dtype);   // query rows per workgroup of the fp32 MFMA kernel
 hipError_t launch_attn_mfma_bf16(const AttnArgs& a, int64_t grid, hipStream_t stream);
 int bf16_rows_per_workgroup();   // query rows per workgroup of the bf16 MFMA kernel
-hipError_t launch_attn_mfma_bf16w(const AttnArgs& a, int64_t grid, hipStream_t stream);
-int bf16w_rows_per_workgroup();  // query rows per workgroup of the 32-rows-per-wave bf16 kernel
 hipError_t launch_merge(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_tree_build(const TreeArgs& a, hipStream_t stream);
 hipError_t launch_tree_accept(const AcceptArgs& a, hipStream_t stream);
