@@ -533,6 +533,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--no-configs", dest="configs", action="store_false",
                     help="skip the other workloads (c3, c5, the q_len-1 probe) after the c4 headline")
+    ap.add_argument("--attn-only", action="store_true",
+                    help="time the verify step only (no builder, tail, acceptance, projection, FP8, iteration "
+                         "or other-workload sections): for profiler and counter runs")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="instead of the bench, run N launches of a plain copy of the cache bytes "
@@ -616,14 +619,15 @@ def main():
             "kernel_source_hash": res["kernel_source_hash"],
         },
     }
-    out["tree_build"] = time_tree_builder(dd, hip, stream, dev, w.B, w.Q)
-    out["tail_mode"] = time_tail_mode(dd, hip, stream, r)
-    out["tree_accept"] = time_tree_accept(dd, hip, stream, r)
-    out["neighbour"] = time_neighbour(dd, hip, stream, r)
-    out["fp8_cache"] = time_fp8_cache(dd, hip, stream, r, res["flops"])
-    out["iteration"] = time_iteration(dd, hip, stream, r)
-    out["iteration_growing_prefix"] = time_iteration(dd, hip, stream, r, grow=True)
-    if args.configs and args.config == "c4" and not args.q_len:
+    if not args.attn_only:
+        out["tree_build"] = time_tree_builder(dd, hip, stream, dev, w.B, w.Q)
+        out["tail_mode"] = time_tail_mode(dd, hip, stream, r)
+        out["tree_accept"] = time_tree_accept(dd, hip, stream, r)
+        out["neighbour"] = time_neighbour(dd, hip, stream, r)
+        out["fp8_cache"] = time_fp8_cache(dd, hip, stream, r, res["flops"])
+        out["iteration"] = time_iteration(dd, hip, stream, r)
+        out["iteration_growing_prefix"] = time_iteration(dd, hip, stream, r, grow=True)
+    if args.configs and not args.attn_only and args.config == "c4" and not args.q_len:
         # the other workloads, each in its own timed region (the headline above stays c4)
         out["configs"] = {}
         del r
