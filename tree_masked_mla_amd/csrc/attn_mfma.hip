@@ -354,6 +354,18 @@ __device__ __forceinline__ void sm_pv_slot(f32x4 (&oacc)[16], const f32x4* sx_mi
     }
 }
 
+// Barrier at the score swap.  Row-half mode meets it once its LDS work is done,
+// so the next tile's loads stay in flight across it (__syncthreads would first
+// wait for them, and P.V would start only after the next tile had landed).  The
+// usual mode keeps __syncthreads, which measured faster there.
+template <bool kHv>
+__device__ __forceinline__ void swap_barrier() {
+    if constexpr (kHv)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+        __syncthreads();
+}
+
 // One workgroup's work; HALF is the wave's half of the pair (wave-uniform);
 // kHv selects row-half mode.
 template <int KV, int HALF, bool kHv>
@@ -415,6 +427,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
     const TileOffsets to = tile_offsets(g, n);
     f32x4* sx_mine = &sm.sx[wave][0][0];
     const f32x4* sx_partner = &sm.sx[wave ^ 1][0][0];
+    // Row-half mode with at most 16 query rows: waves 4..7 are idle, and on fp32
+    // caches they issue every tile load (their own rows and those of waves 0..3)
+    // right after the loop-top barrier, so the computing waves issue none.
+    const bool helpers = KV == DDTV_F32 && kHv && a.R <= 16;
     // A pair whose 16 rows all lie beyond the batch row's H*Q query rows (small
     // trees, few heads) only loads its share of the tiles and meets the barriers:
     // its matrix work would be discarded, and skipping it frees the SIMDs for the
@@ -425,12 +441,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
             __syncthreads();
             const bool more = it + 1 < ntiles;
             if (more) {
-                if (KV == DDTV_F32)
-                    issue_tile_f32(sm.kv[(it + 1) & 1], a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, wave, lane);
-                else
+                if (KV == DDTV_F32) {
+                    f32x4* nb = sm.kv[(it + 1) & 1];
+                    const int t1 = kv_lo + (it + 1) * kTile;
+                    if (helpers) issue_tile_f32(nb, a, kv_base, t1, kv_len - 1, wave - 4, lane);
+                    issue_tile_f32(nb, a, kv_base, t1, kv_len - 1, wave, lane);
+                } else
                     load_tile_narrow<KV>(stage, a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, tid);
             }
-            __syncthreads();
+            swap_barrier<kHv>();
             if (KV != DDTV_F32 && more) store_tile_narrow<KV>(sm.kv[(it + 1) & 1], stage, tid);
         }
         return;   // no rows to write
@@ -440,7 +459,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         __syncthreads();                                  // tile `it` is in LDS
         const bool more = it + 1 < ntiles;
         auto issue = [&]() {
-            if (more) {
+            if (more && !helpers) {
                 if (KV == DDTV_F32)
                     issue_tile_f32(sm.kv[(it + 1) & 1], a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, wave, lane);
                 else
@@ -449,7 +468,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         };
         const char* Kb = reinterpret_cast<const char*>(sm.kv[it & 1]);
         qk_slot<HALF, kHv>(Kb, to, qreg, sx_mine, lane, issue, rh);
-        __syncthreads();                                  // partner's partial scores are in LDS
+        swap_barrier<kHv>();                              // partner's partial scores are in LDS
         sm_pv_slot<HALF, kHv>(oacc, sx_mine, sx_partner, Kb, to, m_run, l_lane, mrow, g, n, lane, kv_lo + it * kTile,
                               P, kv_hi, rh);
         if (KV != DDTV_F32 && more) store_tile_narrow<KV>(sm.kv[(it + 1) & 1], stage, tid);
