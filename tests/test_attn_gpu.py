@@ -120,6 +120,23 @@ def test_split_count_invariance():
         assert np.abs(o - outs[0]).max() < 1e-5
 
 
+# Many partials on few rows: the merge shares a row's partials among 2, 4 or 8
+# thread groups and combines their results in LDS (test_split_count_invariance
+# covers 1 and 2 groups on c3).
+@pytest.mark.parametrize("B,H,Q,prefix,split_len,path", [
+    (2, 16, 1, [20000, 3], 256, 2),    # row-half, 158 partials on the long row: 8 groups, 20 each
+    (1, 16, 4, [9000], 128, 2),        # 64 rows, 71 splits: 8 groups, the last one short
+    (2, 8, 4, [3000, 700], 96, 2),     # row-half, 64 partials: 4 groups of 16
+    (1, 4, 4, [2100], 64, 1),          # vector path, 34 splits: 4 groups
+])
+def test_merge_partial_groups(B, H, Q, prefix, split_len, path):
+    w = wl.make_workload(f"mg{B}x{H}x{Q}", 7000 + B * 100 + H * 10 + Q, B=B, H=H, Q=Q, prefix=prefix,
+                         tree="uniform")
+    r, _, _ = check_full(w, path=path, split_len=split_len,
+                         what=f"merge groups B{B} H{H} Q{Q} P{prefix} split {split_len}")
+    assert r.plan()[2] == split_len
+
+
 def test_path_invariance():
     """q_len = 16 sits on the dispatch boundary: both paths must agree with the oracle."""
     w = wl.make_workload("q16", 3016, B=2, H=8, Q=16, prefix=[40, 130], tree="uniform")
