@@ -58,6 +58,58 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+CALIB_LIB = os.path.join(ROOT, "tree_masked_mla_amd", "libddtv_calib.so")
+
+
+def read_ceiling(hip, stream, buf, workgroups, reps=10, warmup=2):
+    """What a bare read stream reaches on this GPU over the device tensor `buf`
+    (read once per launch, whole units per workgroup): the calibration library's
+    LDS stream (72 KiB tiles by global_load_lds, the attention kernel's way of
+    streaming its cache, without the math) and its register stream, one 512-thread
+    workgroup per CU.  Context for memory-bound lines: the roofline's peak stays
+    the published 8 TB/s."""
+    import torch
+    if not os.path.exists(CALIB_LIB):
+        raise FileNotFoundError(f"{CALIB_LIB} not found; build it with `python -m tree_masked_mla_amd.build`")
+    lib = ctypes.CDLL(CALIB_LIB)   # torch is loaded already: one HIP runtime in the process
+    f = lib.ddtv_calib_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.POINTER(ctypes.c_int64)]
+    f.restype = ctypes.c_int
+    sink = torch.empty(workgroups * 512, dtype=torch.float32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    out = {"kind": "bare read stream, one 512-thread workgroup per CU over a contiguous share of the "
+                   "benchmarked cache's latent array", "workgroups": workgroups}
+    for mode, name in ((0, "lds_dma_72KiB_tiles"), (1, "vgpr_16B_loads")):
+        nread = ctypes.c_int64()
+
+        def launch():
+            rc = f(buf.data_ptr(), nbytes, mode, sink.data_ptr(), workgroups, stream, ctypes.byref(nread))
+            assert rc == 0, f"ddtv_calib_stream_read returned {rc}"
+        for _ in range(warmup):
+            launch()
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, stream)
+        for _ in range(reps):
+            launch()
+        hip.record(e1, stream)
+        ms = hip.elapsed_ms(e0, e1) / reps
+        out[name] = {"gbps": round(nread.value / (ms / 1e3) / 1e9, 1), "us": round(ms * 1e3, 2),
+                     "bytes_read": nread.value}
+    out["gbps"] = max(out["lds_dma_72KiB_tiles"]["gbps"], out["vgpr_16B_loads"]["gbps"])
+    out["pct_of_peak"] = round(100.0 * out["gbps"] / HBM_PEAK_GBPS, 2)
+    return out
+
+
+def with_ceiling(roof, ceiling):
+    """A memory-bound roofline also states its fraction of the measured read ceiling."""
+    roof = dict(roof)
+    if roof["bound"] == "hbm" and ceiling:
+        roof["read_ceiling_gbps"] = ceiling["gbps"]
+        roof["frac_of_read_ceiling"] = round(roof["achieved"] / ceiling["gbps"], 4)
+    return roof
+
+
 # ----------------------------------------------------------------------------- HIP events (ctypes)
 class Hip:
     def __init__(self):
@@ -585,6 +637,8 @@ def main():
     traffic_name = None if args.q_len else args.config
     r, res = measure(dd, hip, stream, w, K, args.warmup, args.path, args.split_len, args.wg_order, dev,
                      traffic_name)
+    ceiling = read_ceiling(hip, stream, r.ckv, torch.cuda.get_device_properties(dev).multi_processor_count)
+    res["roofline"] = with_ceiling(res["roofline"], ceiling)
     ms_step, attn_avg_ms = res["ms_per_step"], res["attn_ms"]
     tokens = w.B * w.Q
     value = tokens / (ms_step / 1e3)
@@ -614,6 +668,7 @@ def main():
         "attn_kernel_us": round(attn_avg_ms * 1e3, 2),
         "step_us": round(ms_step * 1e3, 2),
         "host_wall_ms_per_step": round(res["host_ms_per_step"], 4),
+        "hbm_read_ceiling": ceiling,
         "roofline": {
             **res["roofline"],
             "traffic": res["traffic"],
@@ -644,6 +699,7 @@ def main():
             log(f"generating {name}: {d}")
             wc = wl.config(base, Q=q_len) if q_len else wl.config(base)
             rc_, res_c = measure(dd, hip, stream, wc, steps, args.warmup, dev=dev, traffic_name=name)
+            res_c["roofline"] = with_ceiling(res_c["roofline"], ceiling)
             out["configs"][name] = config_entry(name, wc, d, res_c, steps)
             del rc_
             torch.cuda.empty_cache()

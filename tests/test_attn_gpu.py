@@ -53,7 +53,7 @@ def test_small_configs(name, path):
     check_full(wl.config(name), path=path)
 
 
-@pytest.mark.parametrize("path", [0, 2])
+@pytest.mark.parametrize("path", [0, 1, 2])
 def test_c2_chain_is_causal(path):
     """The chain variant must equal causal attention; the oracle's equality with
     causal SDPA is pinned on the CPU, so parity with the oracle carries it."""

@@ -59,6 +59,18 @@ class ddtv_opts(ctypes.Structure):
 _lib = None
 
 
+def share_hip_runtime_with_torch() -> None:
+    """Import torch (when installed) before any of this package's HIP libraries is
+    loaded.  torch ships its own copy of the HIP runtime under the same soname as
+    the system's: whichever loads first serves the library, and a process that
+    loads the library first ends up holding two runtimes, the library's blind to
+    the device memory (and, on some drivers, the devices) the other one owns."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+
+
 def load(path: str = LIB_PATH):
     """Load libddtv.so (once) and declare its signatures."""
     global _lib
@@ -66,6 +78,7 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise DdtvLibraryMissing(f"{path} not found; build it with `python -m tree_masked_mla_amd.build`")
+    share_hip_runtime_with_torch()
     lib = ctypes.CDLL(path)
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     VP, OP = ctypes.POINTER(ddtv_vis), ctypes.POINTER(ddtv_opts)

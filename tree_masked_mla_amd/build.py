@@ -1,4 +1,5 @@
-"""Build libddtv.so (HIP, gfx950 only) in-tree with hipcc.
+"""Build libddtv.so (HIP, gfx950 only) in-tree with hipcc, and libddtv_calib.so,
+the benchmark's HBM read-stream calibration (not part of the verify path).
 
     python -m tree_masked_mla_amd.build
 
@@ -19,9 +20,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libddtv.so")
+CALIB_LIB = os.path.join(PKG, "libddtv_calib.so")
 
 SOURCES = ["api.hip", "visibility.hip", "attn_valu.hip", "attn_mfma.hip", "attn_mfma_bf16.hip", "merge.hip",
            "tree_build.hip", "tree_accept.hip", "tail.hip", "neighbour.hip"]
+CALIB_SOURCES = ["calib_stream.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -46,19 +49,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link the shared library.  Always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link both shared libraries.  Always rebuilds."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CALIB_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in CALIB_SOURCES], CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
 
 
