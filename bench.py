@@ -61,13 +61,17 @@ def log(msg):
 CALIB_LIB = os.path.join(ROOT, "tree_masked_mla_amd", "libddtv_calib.so")
 
 
-def read_ceiling(hip, stream, buf, workgroups, reps=10, warmup=2):
-    """What a bare read stream reaches on this GPU over the device tensor `buf`
-    (read once per launch, whole units per workgroup): the calibration library's
-    LDS stream (72 KiB tiles by global_load_lds, the attention kernel's way of
-    streaming its cache, without the math) and its register stream, one 512-thread
-    workgroup per CU.  Context for memory-bound lines: the roofline's peak stays
-    the published 8 TB/s."""
+CEILING_BYTES = 512 << 20   # well past every cache level (MI355X: 4 MiB L2 per XCD, 256 MiB MALL)
+
+
+def read_ceiling(hip, stream, dev, workgroups, nbytes=CEILING_BYTES, reps=10, warmup=2):
+    """What a bare read stream reaches on this GPU over a zeroed `nbytes` device
+    buffer (read once per launch, whole units per workgroup): the calibration
+    library's LDS stream (72 KiB tiles by global_load_lds, the attention kernel's
+    way of streaming its cache, without the math) and its register stream, one
+    512-thread workgroup per CU.  A property of the GPU, not of the workload, so it
+    is measured on its own buffer.  Context for memory-bound lines: the roofline's
+    peak stays the published 8 TB/s."""
     import torch
     if not os.path.exists(CALIB_LIB):
         raise FileNotFoundError(f"{CALIB_LIB} not found; build it with `python -m tree_masked_mla_amd.build`")
@@ -76,10 +80,10 @@ def read_ceiling(hip, stream, buf, workgroups, reps=10, warmup=2):
     f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                   ctypes.POINTER(ctypes.c_int64)]
     f.restype = ctypes.c_int
-    sink = torch.empty(workgroups * 512, dtype=torch.float32, device=buf.device)
-    nbytes = buf.numel() * buf.element_size()
-    out = {"kind": "bare read stream, one 512-thread workgroup per CU over a contiguous share of the "
-                   "benchmarked cache's latent array", "workgroups": workgroups}
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.empty(workgroups * 512, dtype=torch.float32, device=dev)
+    out = {"kind": f"bare read stream of a {nbytes >> 20} MiB buffer, one 512-thread workgroup per CU over a "
+                   "contiguous share", "workgroups": workgroups}
     for mode, name in ((0, "lds_dma_72KiB_tiles"), (1, "vgpr_16B_loads")):
         nread = ctypes.c_int64()
 
@@ -98,13 +102,15 @@ def read_ceiling(hip, stream, buf, workgroups, reps=10, warmup=2):
                      "bytes_read": nread.value}
     out["gbps"] = max(out["lds_dma_72KiB_tiles"]["gbps"], out["vgpr_16B_loads"]["gbps"])
     out["pct_of_peak"] = round(100.0 * out["gbps"] / HBM_PEAK_GBPS, 2)
+    del buf, sink
+    torch.cuda.empty_cache()
     return out
 
 
 def with_ceiling(roof, ceiling):
     """A memory-bound roofline also states its fraction of the measured read ceiling."""
     roof = dict(roof)
-    if roof["bound"] == "hbm" and ceiling:
+    if roof["bound"] == "hbm" and ceiling and ceiling["gbps"] > 0:
         roof["read_ceiling_gbps"] = ceiling["gbps"]
         roof["frac_of_read_ceiling"] = round(roof["achieved"] / ceiling["gbps"], 4)
     return roof
@@ -637,7 +643,7 @@ def main():
     traffic_name = None if args.q_len else args.config
     r, res = measure(dd, hip, stream, w, K, args.warmup, args.path, args.split_len, args.wg_order, dev,
                      traffic_name)
-    ceiling = read_ceiling(hip, stream, r.ckv, torch.cuda.get_device_properties(dev).multi_processor_count)
+    ceiling = read_ceiling(hip, stream, dev, torch.cuda.get_device_properties(dev).multi_processor_count)
     res["roofline"] = with_ceiling(res["roofline"], ceiling)
     ms_step, attn_avg_ms = res["ms_per_step"], res["attn_ms"]
     tokens = w.B * w.Q
