@@ -601,6 +601,9 @@ def main():
                     help="time the verify step only (no builder, tail, acceptance, projection, FP8, iteration "
                          "or other-workload sections): for profiler and counter runs")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--read-calibration", type=int, default=0,
+                    help="instead of the bench, run N launches of each read-stream calibration kernel over a "
+                         "512 MiB buffer (known bytes read, for scaling rocprofv3 FETCH_SIZE)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="instead of the bench, run N launches of a plain copy of the cache bytes "
                          "(for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -619,6 +622,15 @@ def main():
     dd.load()   # fails loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.read_calibration:
+        hip = Hip()
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        c = read_ceiling(hip, stream, dev, torch.cuda.get_device_properties(dev).multi_processor_count,
+                         reps=args.read_calibration, warmup=0)
+        torch.cuda.synchronize()
+        print(json.dumps({"read_calibration": c, "launches_per_kernel": args.read_calibration}))
+        return
 
     desc = wl.DESCRIPTIONS[args.config]
     if args.q_len:
