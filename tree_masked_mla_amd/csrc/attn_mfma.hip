@@ -36,7 +36,9 @@
 //    The two halves leave two partials per split, combined by the merge pass like
 //    any other split.  With 16 rows this puts pairs 0 and 1 (waves 0..3, one per
 //    SIMD) to work where otherwise one pair (two SIMDs) would do all the matrix
-//    work of the tile.
+//    work of the tile; the idle waves 4..7 then issue every tile load, and the
+//    score-swap barrier waits for LDS work only, so the next tile streams in
+//    during P.V.
 //  * fp32 caches go HBM->LDS with global_load_lds_dwordx4 (no VGPR staging),
 //    double buffered; bf16 and FP8 caches are widened exactly to fp32 through
 //    VGPRs on the way in.
