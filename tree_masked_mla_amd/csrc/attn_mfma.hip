@@ -281,13 +281,22 @@ __device__ __forceinline__ void qk_slot(const char* Kb, const TileOffsets& to, c
 
 // Full scores of the tile starting at cache position t0 (own partial and the
 // partner's, both from LDS), online softmax, then O += P V over this wave's 256 dims.
-// Row-half mode: only the 16 cache rows of half rh.
-template <int HALF, bool kHv>
+// Row-half mode: only the 16 cache rows of half rh.  kPF pins the value reads
+// one step ahead (off for the widened bf16 cache, whose registers it would spill).
+template <int HALF, bool kHv, bool kPF>
 __device__ __forceinline__ void sm_pv_slot(f32x4 (&oacc)[16], const f32x4* sx_mine, const f32x4* sx_partner,
                                            const char* Kb, const TileOffsets& to, float& m_run, float& l_lane,
                                            const uint32_t* mrow, int g, int n, int lane, int t0, int P,
                                            int kv_hi, int rh) {
     constexpr int NE = kHv ? 4 : 8;   // scores per lane: cache rows 16 (e >> 2) + 4g + (e & 3), or 16 rh + 4g + e
+    // value operands of step e (cache row vr(e), this wave's 256 dims); read one
+    // step ahead of their MFMAs, the first step's before the softmax arithmetic
+    auto vread = [&](int e, f32x4 (&v)[4]) {
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+            v[T] = lds16(Kb, to.voff[e & 3] + (kHv ? rh : (e >> 2)) * 32768 + 256 * (4 * HALF + T));
+    };
+    f32x4 vf[4];
     float sv[8];
     {
         const f32x4 a0 = sx_mine[lane] + sx_partner[lane];
@@ -299,6 +308,8 @@ __device__ __forceinline__ void sm_pv_slot(f32x4 (&oacc)[16], const f32x4* sx_mi
             for (int e = 0; e < 4; ++e) sv[4 + e] = a1[e];
         }
     }
+    vread(0, vf);
+    if constexpr (kPF) __builtin_amdgcn_sched_barrier(0);   // (the scheduler would sink the reads to their MFMAs)
     const bool full = (t0 + kTile <= P) && (t0 + kTile <= kv_hi);
     float tmax = -INFINITY;
 #pragma unroll
@@ -339,19 +350,20 @@ __device__ __forceinline__ void sm_pv_slot(f32x4 (&oacc)[16], const f32x4* sx_mi
     }
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
-        const int vr = (e >> 2) * 16 + 4 * g + (e & 3);
         const float pv = sv[e];
-        f32x4 vf[4];
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-            vf[T] = lds16(Kb, to.voff[e & 3] + (kHv ? rh : (e >> 2)) * 32768 + 256 * (4 * HALF + T));
-        (void)vr;
+        f32x4 vn[4];
+        if (e + 1 < NE) vread(e + 1, vn);
+        if constexpr (kPF) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
             oacc[4 * T + 0] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vf[T][0], oacc[4 * T + 0], 0, 0, 0);
             oacc[4 * T + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vf[T][1], oacc[4 * T + 1], 0, 0, 0);
             oacc[4 * T + 2] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vf[T][2], oacc[4 * T + 2], 0, 0, 0);
             oacc[4 * T + 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vf[T][3], oacc[4 * T + 3], 0, 0, 0);
+        }
+        if (e + 1 < NE) {
+#pragma unroll
+            for (int T = 0; T < 4; ++T) vf[T] = vn[T];
         }
     }
 }
@@ -471,7 +483,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         const char* Kb = reinterpret_cast<const char*>(sm.kv[it & 1]);
         qk_slot<HALF, kHv>(Kb, to, qreg, sx_mine, lane, issue, rh);
         swap_barrier<kHv>();                              // partner's partial scores are in LDS
-        sm_pv_slot<HALF, kHv>(oacc, sx_mine, sx_partner, Kb, to, m_run, l_lane, mrow, g, n, lane, kv_lo + it * kTile,
+        sm_pv_slot<HALF, kHv, KV != DDTV_BF16>(oacc, sx_mine, sx_partner, Kb, to, m_run, l_lane, mrow, g, n, lane, kv_lo + it * kTile,
                               P, kv_hi, rh);
         if (KV != DDTV_F32 && more) store_tile_narrow<KV>(sm.kv[(it + 1) & 1], stage, tid);
     }
