@@ -227,6 +227,8 @@ def test_edge_shapes_bf16_mfma(B, H, Q, prefix):
     (2, 5, 5, [63, 64], 128),          # 25 rows: pairs 2, 3 hold rows 16..24
     (2, 1, 9, [40, 5], 0),             # 9 rows (the matrix path forced below 16)
     (3, 3, 1, [300, 31, 0], 96),       # 3 rows, ragged tails, a row with no prefix
+    (2, 16, 1, [100, 3], 32),          # 16 rows, one-tile splits (the idle waves load nothing ahead)
+    (1, 8, 2, [500], 0),               # 16 rows from a two-node tree: idle-wave loads and tree masks
 ])
 def test_row_half_mode(kv_dtype, path, B, H, Q, prefix, split_len):
     if path == 0 and Q * H < 16:
