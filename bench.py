@@ -193,9 +193,10 @@ def load_traffic(config_name, kernel_hash):
 
 
 def load_counters(config_name, kernel_hash):
-    """Matrix-pipe busy fraction per SIMD of the attention kernel from a committed
-    rocprofv3 counter summary (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE),
-    or None when absent or taken on other kernel sources."""
+    """The attention kernel's committed rocprofv3 counter summary: matrix-pipe busy
+    fraction per SIMD (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE) and executed
+    matrix flops per launch (SQ_INSTS_VALU_MFMA_MOPS_* x 512), or None when absent
+    or taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", f"counters_attn_{config_name}.json")
     if not os.path.exists(path):
         return None
@@ -203,7 +204,7 @@ def load_counters(config_name, kernel_hash):
         t = json.load(f)
     if t.get("kernel_source_hash") != kernel_hash:
         return None
-    return t.get("mfma_busy_per_simd")
+    return t
 
 
 # ----------------------------------------------------------------------------- CPU baseline (oracle)
@@ -560,10 +561,17 @@ def measure(dd, hip, stream, w, K, warmup, path=0, split_len=0, wg_order=0, dev=
         "dtype": "bf16" if bf16_mma else "f32", "kernel": kernel, "kernel_source_hash": khash,
         "flops": flops, "nbytes": nbytes, "vis_pairs": vis_pairs, "roofline": roof,
         "traffic": load_traffic(traffic_name, khash) if traffic_name else None,
-        "mfma_busy": load_counters(traffic_name, khash) if traffic_name else None,
+        "counters": load_counters(traffic_name, khash) if traffic_name else None,
         "plan": {"path": ppath, "split_len": psplit, "n_split": pn, "workgroups": pwgs,
                  "wg_order": {1: "xcd-local", 2: "spread"}.get(porder, porder)},
     }
+    ctr = res.pop("counters")
+    res["mfma_busy"] = ctr.get("mfma_busy_per_simd") if ctr else None
+    ex = ctr.get("executed_flops_per_launch") if ctr else None
+    # executed matrix flops (counters) over the same events' kernel time: the
+    # algorithmic figure plus products spent on masked positions and padding
+    res["mfma_executed"] = ({"flops_per_launch": ex, "tflops": round(ex / (attn_ms / 1e3) / 1e12, 3),
+                             "over_algorithmic": ctr.get("executed_over_algorithmic_flops")} if ex else None)
     return r, res
 
 
@@ -577,6 +585,7 @@ def config_entry(name, w, desc, res, steps):
             "kernel": res["kernel"], "kernel_us": round(res["attn_ms"] * 1e3, 2),
             "step_us": round(res["ms_per_step"] * 1e3, 2), "tokens_per_s": round(res["tokens_per_s"], 1),
             "hbm_gbps": round(res["hbm_gbps"], 2), "roofline": roof, "mfma_busy": res["mfma_busy"],
+            "mfma_executed": res["mfma_executed"],
             "kernel_source_hash": res["kernel_source_hash"], "flops_per_launch": res["flops"],
             "algorithmic_bytes_per_step": res["nbytes"], "plan": res["plan"], "steps": steps}
 
@@ -691,6 +700,7 @@ def main():
             **res["roofline"],
             "traffic": res["traffic"],
             "mfma_busy": res["mfma_busy"],
+            "mfma_executed": res["mfma_executed"],
             "kernel": res["kernel"],
             "flops_per_launch": res["flops"],
             "algorithmic_bytes_per_step": res["nbytes"],
