@@ -59,6 +59,9 @@ def log(msg):
 
 
 CALIB_LIB = os.path.join(ROOT, "tree_masked_mla_amd", "libddtv_calib.so")
+# The other workloads of the line (`configs`) warm up for at least this long, so
+# that their short launches are timed at the steady-state shader clock.
+CONFIG_MIN_WARM_MS = 60.0
 
 
 CEILING_BYTES = 512 << 20   # well past every cache level (MI355X: 4 MiB L2 per XCD, 256 MiB MALL)
@@ -518,10 +521,12 @@ def cpu_baseline(w, budget_s=15.0, max_rows=4096):
                       f"{dt:.1f} s on 1 host core pinned by affinity; tokens/s = rows/s / H"}
 
 
-def measure(dd, hip, stream, w, K, warmup, path=0, split_len=0, wg_order=0, dev=None, traffic_name=None):
-    """Time K verify steps (S1..S7) of workload w after `warmup` untimed ones: the
-    step from events around all K, the attention kernel from events the library
-    records around it on the same stream.  Returns the run and a result dict."""
+def measure(dd, hip, stream, w, K, warmup, path=0, split_len=0, wg_order=0, dev=None, traffic_name=None,
+            min_warm_ms=0.0):
+    """Time K verify steps (S1..S7) of workload w after `warmup` untimed ones (and,
+    with min_warm_ms, more until that much wall time has passed): the step from
+    events around all K, the attention kernel from events the library records
+    around it on the same stream.  Returns the run and a result dict."""
     import workloads as wl
     from tree_masked_mla_amd.runner import DeviceRun
     r = DeviceRun(w, device=dev, path=path, split_len=split_len, want_lse=True, wg_order=wg_order)
@@ -532,6 +537,16 @@ def measure(dd, hip, stream, w, K, warmup, path=0, split_len=0, wg_order=0, dev=
     for _ in range(warmup):
         r.step(stream)
     import torch
+    torch.cuda.synchronize()
+    # Short steps (~0.1 ms) reach the GPU's steady-state shader clock only after
+    # tens of milliseconds of work (c3: 95.9 -> 89.3 us per attention launch).
+    n_warm = warmup
+    t_w0 = time.perf_counter()
+    while (time.perf_counter() - t_w0) * 1e3 < min_warm_ms:
+        r.step(stream)
+        n_warm += 1
+        if n_warm % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     t_host0 = time.perf_counter()
     hip.record(ev0, stream)
@@ -558,7 +573,7 @@ def measure(dd, hip, stream, w, K, warmup, path=0, split_len=0, wg_order=0, dev=
     roof = roofline_bound(valu, flops, attn_nbytes, attn_ms, PEAK_TFLOPS[peak_key])
     roof["bytes_per_launch"] = attn_nbytes
     res = {
-        "ms_per_step": ms_step, "attn_ms": attn_ms, "attn_median_ms": attn_med_ms, "host_ms_per_step": (t_host1 - t_host0) * 1e3 / K,
+        "warmup_steps": n_warm, "ms_per_step": ms_step, "attn_ms": attn_ms, "attn_median_ms": attn_med_ms, "host_ms_per_step": (t_host1 - t_host0) * 1e3 / K,
         "tokens_per_s": w.B * w.Q / (ms_step / 1e3), "hbm_gbps": nbytes / (ms_step / 1e3) / 1e9,
         "dtype": "bf16" if bf16_mma else "f32", "kernel": kernel, "kernel_source_hash": khash,
         "flops": flops, "nbytes": nbytes, "vis_pairs": vis_pairs, "roofline": roof,
@@ -590,7 +605,8 @@ def config_entry(name, w, desc, res, steps):
             "hbm_gbps": round(res["hbm_gbps"], 2), "roofline": roof, "mfma_busy": res["mfma_busy"],
             "mfma_executed": res["mfma_executed"],
             "kernel_source_hash": res["kernel_source_hash"], "flops_per_launch": res["flops"],
-            "algorithmic_bytes_per_step": res["nbytes"], "plan": res["plan"], "steps": steps}
+            "algorithmic_bytes_per_step": res["nbytes"], "plan": res["plan"], "steps": steps,
+            "warmup_steps": res["warmup_steps"]}
 
 
 # ----------------------------------------------------------------------------- main
@@ -730,7 +746,8 @@ def main():
             d = wl.DESCRIPTIONS[base] + (f" [decode probe: q_len {q_len}]" if q_len else "")
             log(f"generating {name}: {d}")
             wc = wl.config(base, Q=q_len) if q_len else wl.config(base)
-            rc_, res_c = measure(dd, hip, stream, wc, steps, args.warmup, dev=dev, traffic_name=name)
+            rc_, res_c = measure(dd, hip, stream, wc, steps, args.warmup, dev=dev, traffic_name=name,
+                                 min_warm_ms=CONFIG_MIN_WARM_MS)
             res_c["roofline"] = with_ceiling(res_c["roofline"], ceiling)
             out["configs"][name] = config_entry(name, wc, d, res_c, steps)
             del rc_
