@@ -482,10 +482,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         };
         const char* Kb = reinterpret_cast<const char*>(sm.kv[it & 1]);
         qk_slot<HALF, kHv>(Kb, to, qreg, sx_mine, lane, issue, rh);
+        // Narrow caches: the next tile goes into its buffer (free since the loop-top
+        // barrier) before the score swap, where the waves that finish their scores
+        // first would otherwise wait for the others.
+        if (KV != DDTV_F32 && more) store_tile_narrow<KV>(sm.kv[(it + 1) & 1], stage, tid);
         swap_barrier<kHv>();                              // partner's partial scores are in LDS
         sm_pv_slot<HALF, kHv, KV != DDTV_BF16>(oacc, sx_mine, sx_partner, Kb, to, m_run, l_lane, mrow, g, n, lane, kv_lo + it * kTile,
                               P, kv_hi, rh);
-        if (KV != DDTV_F32 && more) store_tile_narrow<KV>(sm.kv[(it + 1) & 1], stage, tid);
     }
 
     // ---- epilogue: output rows pair*16 + 4g + j of the tile, dims 256*HALF + 64T + 4n + (0..3)
