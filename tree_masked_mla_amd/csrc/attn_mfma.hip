@@ -368,13 +368,13 @@ __device__ __forceinline__ void sm_pv_slot(f32x4 (&oacc)[16], const f32x4* sx_mi
     }
 }
 
-// Barrier at the score swap.  Row-half mode meets it once its LDS work is done,
-// so the next tile's loads stay in flight across it (__syncthreads would first
-// wait for them, and P.V would start only after the next tile had landed).  The
-// usual mode keeps __syncthreads, which measured faster there.
-template <bool kHv>
+// Barrier at the score swap.  With tile loads in flight it waits for LDS work
+// only, so the loads stay in flight across it (__syncthreads would first wait for
+// them, and P.V would start only after the next tile had landed).  Narrow caches
+// in the usual mode keep __syncthreads.
+template <bool kLdsOnly>
 __device__ __forceinline__ void swap_barrier() {
-    if constexpr (kHv)
+    if constexpr (kLdsOnly)
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else
         __syncthreads();
@@ -445,6 +445,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
     // caches they issue every tile load (their own rows and those of waves 0..3)
     // right after the loop-top barrier, so the computing waves issue none.
     const bool helpers = KV == DDTV_F32 && kHv && a.R <= 16;
+    // Usual mode, fp32 cache: each SIMD holds waves w and w + 4, and the older
+    // waves 0..3 finish their scores thousands of cycles before 4..7, then wait at
+    // the score swap.  They issue the whole next tile there (their rows and those
+    // of waves 4..7), so the waves on the critical path issue no loads.
+    constexpr bool early_issue = KV == DDTV_F32 && !kHv;
     // A pair whose 16 rows all lie beyond the batch row's H*Q query rows (small
     // trees, few heads) only loads its share of the tiles and meets the barriers:
     // its matrix work would be discarded, and skipping it frees the SIMDs for the
@@ -473,7 +478,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         __syncthreads();                                  // tile `it` is in LDS
         const bool more = it + 1 < ntiles;
         auto issue = [&]() {
-            if (more && !helpers) {
+            if (more && !helpers && !early_issue) {
                 if (KV == DDTV_F32)
                     issue_tile_f32(sm.kv[(it + 1) & 1], a, kv_base, kv_lo + (it + 1) * kTile, kv_len - 1, wave, lane);
                 else
@@ -482,11 +487,17 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         };
         const char* Kb = reinterpret_cast<const char*>(sm.kv[it & 1]);
         qk_slot<HALF, kHv>(Kb, to, qreg, sx_mine, lane, issue, rh);
+        if (early_issue && more && wave < 4) {
+            f32x4* nb = sm.kv[(it + 1) & 1];
+            const int t1 = kv_lo + (it + 1) * kTile;
+            issue_tile_f32(nb, a, kv_base, t1, kv_len - 1, wave, lane);
+            issue_tile_f32(nb, a, kv_base, t1, kv_len - 1, wave + 4, lane);
+        }
         // Narrow caches: the next tile goes into its buffer (free since the loop-top
         // barrier) before the score swap, where the waves that finish their scores
         // first would otherwise wait for the others.
         if (KV != DDTV_F32 && more) store_tile_narrow<KV>(sm.kv[(it + 1) & 1], stage, tid);
-        swap_barrier<kHv>();                              // partner's partial scores are in LDS
+        swap_barrier<kHv || early_issue>();               // partner's partial scores are in LDS
         sm_pv_slot<HALF, kHv, KV != DDTV_BF16>(oacc, sx_mine, sx_partner, Kb, to, m_run, l_lane, mrow, g, n, lane, kv_lo + it * kTile,
                               P, kv_hi, rh);
     }
