@@ -565,10 +565,9 @@ def measure(dd, hip, stream, w, K, warmup, path=0, split_len=0, wg_order=0, dev=
     peak_key = "bf16-mfma" if bf16_mma else ("f32-valu" if valu else "f32-mfma")
     kernel = "attn_mfma_bf16_kernel" if bf16_mma else ("attn_valu_kernel" if valu else "attn_mfma_kernel")
     khash = kernel_source_hash(kernel)
-    # With splits, or in row-half mode (fp32 matrix path, at most 32 query rows per
-    # batch row: two partials per split, always merged), the merge kernel writes the
-    # output and lse; the attention kernel's roofline leaves those bytes out.
-    merged = pn > 1 or (not valu and not bf16_mma and w.Q * w.H <= 32)
+    # With splits the merge kernel writes the output and lse; the attention
+    # kernel's roofline then leaves those bytes out.
+    merged = pn > 1
     attn_nbytes = nbytes - (w.B * w.Q * w.H * (512 + 1) * 4 if merged else 0)
     roof = roofline_bound(valu, flops, attn_nbytes, attn_ms, PEAK_TFLOPS[peak_key])
     roof["bytes_per_launch"] = attn_nbytes

@@ -256,8 +256,9 @@ def test_plan_rules(lib):
         assert rc == 0 and path == want, (Q, H, path)
     vis = fake_vis(B=1, Q=9, prefix=(100,))
     assert dd.ddtv_plan_info(vis, 8, 0, dd.make_opts(path=dd.DDTV_PATH_MFMA))[1] == dd.DDTV_PATH_MFMA
-    # at most 32 query rows on the matrix path: row-half mode, 32 rows per workgroup and two
-    # partials per split, so a workspace even with one split; bf16 caches keep their own kernel
+    # at most 32 query rows on the matrix path: row-half mode, 32 rows per workgroup, whose
+    # two halves are combined in the workgroup: one partial per split, none with a single
+    # split; bf16 caches keep their own kernel
     def ru(x):
         return (x + 255) // 256 * 256
     for Q, H, path in [(1, 16, 0), (2, 16, 0), (9, 1, dd.DDTV_PATH_MFMA), (4, 8, dd.DDTV_PATH_MFMA_F32)]:
@@ -265,8 +266,9 @@ def test_plan_rules(lib):
         opts = dd.make_opts(path=path) if path else None
         rc, p_, L, ns, wg, order = dd.ddtv_plan_info(vis, H, 0, opts)
         assert rc == 0 and p_ == dd.DDTV_PATH_MFMA and wg == 2 * ns, (Q, H, p_, wg, ns)
-        rows = 2 * 2 * ns * Q * H
-        assert dd.ddtv_workspace_bytes(vis, H, 0, opts) == ru(rows * 512 * 4) + ru(rows * 8), (Q, H)
+        rows = 2 * ns * Q * H
+        want = ru(rows * 512 * 4) + ru(rows * 8) if ns > 1 else 0
+        assert dd.ddtv_workspace_bytes(vis, H, 0, opts) == want, (Q, H)
     vis = fake_vis(B=2, Q=1, prefix=(1000, 3))
     rc, p_, L, ns, wg, order = dd.ddtv_plan_info(vis, 16, dd.DDTV_BF16)
     rows = 2 * ns * 16                                   # one partial per split
@@ -279,14 +281,16 @@ def test_plan_rules(lib):
         rows = 2 * ns * 33
         want = ru(rows * 2048) + ru(rows * 8) if ns > 1 else 0
         assert rc == 0 and wg == 2 * ns and dd.ddtv_workspace_bytes(vis, 11, 0, opts) == want, (L, ns)
-    # 32 rows on the same trees: row-half mode, two partials per split even with a single split
+    # 32 rows on the same trees: row-half mode (one workgroup per split instead of two),
+    # one partial per split, none with a single split
     vis32 = fake_vis(B=2, Q=2, prefix=(1000, 3))
     for L in (128, 2048):
         opts = dd.make_opts(split_len=L)
         rc, p_, L_, ns, wg, order = dd.ddtv_plan_info(vis32, 16, 0, opts)
-        rows = 2 * 2 * ns * 32
+        rows = 2 * ns * 32
+        want = ru(rows * 2048) + ru(rows * 8) if ns > 1 else 0
         assert rc == 0 and wg == 2 * ns, (L, ns, wg)
-        assert dd.ddtv_workspace_bytes(vis32, 16, 0, opts) == ru(rows * 2048) + ru(rows * 8), (L, ns)
+        assert dd.ddtv_workspace_bytes(vis32, 16, 0, opts) == want, (L, ns)
     # a grid past 2^32 work-items is refused before any launch
     big = fake_vis(B=(1 << 16) + 1, Q=256, prefix=np.zeros((1 << 16) + 1, np.int32))
     assert dd.ddtv_plan_info(big, 128, 0)[0] == dd.DDTV_EUNSUPPORTED

@@ -124,9 +124,9 @@ def test_split_count_invariance():
 # thread groups and combines their results in LDS (test_split_count_invariance
 # covers 1 and 2 groups on c3).
 @pytest.mark.parametrize("B,H,Q,prefix,split_len,path", [
-    (2, 16, 1, [20000, 3], 256, 2),    # row-half, 158 partials on the long row: 8 groups, 20 each
+    (2, 16, 1, [20000, 3], 256, 2),    # row-half, 79 partials on the long row: 8 groups, 10 each
     (1, 16, 4, [9000], 128, 2),        # 64 rows, 71 splits: 8 groups, the last one short
-    (2, 8, 4, [3000, 700], 96, 2),     # row-half, 64 partials: 4 groups of 16
+    (2, 8, 4, [3000, 700], 96, 2),     # row-half, 32 partials: 2 groups of 16
     (1, 4, 4, [2100], 64, 1),          # vector path, 34 splits: 4 groups
 ])
 def test_merge_partial_groups(B, H, Q, prefix, split_len, path):
@@ -216,8 +216,8 @@ def test_edge_shapes_bf16_mfma(B, H, Q, prefix):
 
 
 # Batch rows of at most 32 query rows run the matrix kernel in row-half mode: two
-# wave pairs per 16-row group, each over one half of every cache tile, and two
-# partials per split for the merge pass.
+# wave pairs per 16-row group, each over one half of every cache tile, combined in
+# the workgroup (one partial per split; with one split the output directly).
 @pytest.mark.parametrize("kv_dtype,path", [(wl.F32, 0), (wl.F32, 2), (wl.BF16, 3), (wl.FP8, 0)])
 @pytest.mark.parametrize("B,H,Q,prefix,split_len", [
     (2, 16, 1, [1000, 3], 0),          # decode (q_len 1), 16 rows
@@ -241,7 +241,8 @@ def test_row_half_mode(kv_dtype, path, B, H, Q, prefix, split_len):
 
 def test_row_half_mode_single_visible_position_is_exact():
     """Row-half mode on a lone position: one half holds it (p = 1), the other
-    half is empty (weight 0 in the merge), so the output is the row bit for bit."""
+    half is empty (weight 0 when the workgroup combines them), so the output is the
+    row bit for bit."""
     w = wl.make_workload("half-single", 6900, B=1, H=16, Q=1, prefix=0, tree="uniform")
     r, out, lse = run(w, path=2)
     for h in range(w.H):
@@ -360,8 +361,9 @@ def test_c4_full_sampled():
 
 def test_c4_decode_shape_row_half_full_sampled():
     """c4 sizes at q_len 1 (16 query rows per batch row, 262,152 cache rows): the
-    row-half mode in the launch the decode probe times (32 splits, two partials
-    each, merged), on every query row of two batch rows against the oracle."""
+    row-half mode in the launch the decode probe times (many splits, the halves
+    combined in each workgroup, then merged), on every query row of two batch rows
+    against the oracle."""
     say("generate c4 at q_len 1")
     w = wl.config("c4", Q=1)
     bits, _, _ = oracle.build_visibility(w.parent)

@@ -159,7 +159,7 @@ constexpr double kExitCost = 0.02;   // a work item past its row's last split: s
 // lower bound on the makespan, and one that grows with the split count (each
 // split adds its set-up and merge traffic).
 double fluid_bound(const std::vector<int>& kv, int n_rt, int L, int cus, double setup_tiles,
-                   double merge_tiles_per_partial_row_split, int64_t R, int parts_per_split) {
+                   double merge_tiles_per_partial_row_split, int64_t R) {
     int n_split = 1;
     for (int k : kv) n_split = std::max(n_split, (k + L - 1) / L);
     const int full_tiles = (L + kTile - 1) / kTile;
@@ -169,7 +169,7 @@ double fluid_bound(const std::vector<int>& kv, int n_rt, int L, int cus, double 
         const int last = k - (nb - 1) * L;
         work += (double)n_rt * ((double)(nb - 1) * (setup_tiles + full_tiles) + setup_tiles +
                                 (double)((last + kTile - 1) / kTile) + (double)(n_split - nb) * kExitCost);
-        if (nb * parts_per_split > 1) merge += merge_tiles_per_partial_row_split * (double)(nb * parts_per_split) * (double)R;
+        if (nb > 1) merge += merge_tiles_per_partial_row_split * (double)nb * (double)R;
     }
     return work / cus + merge;
 }
@@ -185,7 +185,7 @@ double fluid_bound(const std::vector<int>& kv, int n_rt, int L, int cus, double 
 // simulated run by run.  `bound`: give up (returning at least bound) once the
 // total work alone shows the plan cannot beat it.
 double estimate(const std::vector<int>& kv, int n_rt, int L, int cus, double setup_tiles,
-                double merge_tiles_per_partial_row_split, int64_t R, int parts_per_split, bool spread,
+                double merge_tiles_per_partial_row_split, int64_t R, bool spread,
                 double bound = 1e300) {
     const int per_xcd = std::max(1, std::min(kMaxCusPerXcd, cus / kXcds));
     int n_split = 1;
@@ -193,7 +193,7 @@ double estimate(const std::vector<int>& kv, int n_rt, int L, int cus, double set
     const int64_t G = (int64_t)kv.size() * n_split * n_rt;
     double merge = 0.0;   // each partial row is written, then read by the merge pass
     for (int k : kv) {
-        const int parts = (k + L - 1) / L * parts_per_split;
+        const int parts = (k + L - 1) / L;
         if (parts > 1) merge += merge_tiles_per_partial_row_split * (double)parts * (double)R;
     }
     auto cost = [&](int b, int s) {
@@ -201,7 +201,7 @@ double estimate(const std::vector<int>& kv, int n_rt, int L, int cus, double set
         return len > 0 ? setup_tiles + (double)((len + kTile - 1) / kTile) : kExitCost;
     };
     const double fluid =
-        fluid_bound(kv, n_rt, L, cus, setup_tiles, merge_tiles_per_partial_row_split, R, parts_per_split);
+        fluid_bound(kv, n_rt, L, cus, setup_tiles, merge_tiles_per_partial_row_split, R);
     if (fluid >= bound) return fluid;
     if (G <= (int64_t)per_xcd * kXcds) {   // no XCD gets more items than CUs: all start at once
         int longest = 0;
@@ -387,16 +387,15 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     // cache tile find it in its XCD's L2, so the spread order has to be clearly
     // shorter to be chosen (it is when batch rows differ in length: XCD-local
     // then gives each XCD whole rows).
-    const int hm = p->halves ? 2 : 1;   // partials per split (row-half mode: one per half, always merged)
     auto cost_at = [&](int L, int* order, double bound) {
         if (order_req != DDTV_ORDER_AUTO) {
             *order = order_req;
             return order_req == DDTV_ORDER_SPREAD
-                       ? estimate(kv_sorted, p->n_rt, L, cus, setup, merge_per_row_split, R, hm, true, bound)
-                       : estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, hm, false, bound);
+                       ? estimate(kv_sorted, p->n_rt, L, cus, setup, merge_per_row_split, R, true, bound)
+                       : estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, false, bound);
         }
-        const double local = estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, hm, false, bound);
-        const double spread = estimate(kv_sorted, p->n_rt, L, cus, setup, merge_per_row_split, R, hm, true,
+        const double local = estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, false, bound);
+        const double spread = estimate(kv_sorted, p->n_rt, L, cus, setup, merge_per_row_split, R, true,
                                        std::min(bound, local * 0.98));
         *order = spread < local * 0.98 ? DDTV_ORDER_SPREAD : DDTV_ORDER_XCD_LOCAL;
         return std::min(local, spread);
@@ -421,9 +420,9 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
             int64_t wgs = 0;
             for (int b = 0; b < vis->B; ++b) wgs += (int64_t)((kv[b] + L - 1) / L) * p->n_rt;
             if (wgs > wg_cap && S > 1) break;
-            const int parts_L = ((max_kv + L - 1) / L) * (p->halves ? 2 : 1);
+            const int parts_L = (max_kv + L - 1) / L;
             if (S > 1 && partial_bytes(vis->B, R, parts_L) > ws_cap) break;   // more splits only need more
-            if (S > 1 && fluid_bound(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, hm) >= best * 0.98)
+            if (S > 1 && fluid_bound(kv, p->n_rt, L, cus, setup, merge_per_row_split, R) >= best * 0.98)
                 break;   // its lower bound cannot beat the best by 2 %, nor can more splits'
             int order = DDTV_ORDER_XCD_LOCAL;
             const double e = cost_at(L, &order, best * 0.98);   // a plan must beat the best by 2 %
@@ -443,7 +442,7 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     p->n_split = (max_kv + p->split_len - 1) / p->split_len;
     p->grid = (int64_t)vis->B * p->n_rt * p->n_split;
     if (!grid_fits(p->grid, 512)) return DDTV_EUNSUPPORTED;   // 512 = the largest attention workgroup
-    const int parts = p->n_split * (p->halves ? 2 : 1);   // partials per batch row
+    const int parts = p->n_split;   // partials per batch row
     if (parts > 1 && !grid_fits(((int64_t)vis->B * R + 1) / 2, 256)) return DDTV_EUNSUPPORTED;   // merge
     p->ws_part_o = 0;
     p->ws_part_ml = parts > 1 ? round_up((size_t)vis->B * parts * (size_t)R * kDLat * sizeof(float), 256) : 0;
@@ -529,7 +528,7 @@ ddtv_status launch_verify(const Plan& p, const float* q_abs, const float* q_rope
                                                 : launch_attn_mfma(a, kv_dtype, p.grid, stream);
     if (e != hipSuccess) return DDTV_EDEVICE;
     if (opts && opts->attn_end && hipEventRecord(opts->attn_end, stream) != hipSuccess) return DDTV_EDEVICE;
-    if ((p.n_split > 1 || p.halves) && launch_merge(a, stream) != hipSuccess) return DDTV_EDEVICE;
+    if (p.n_split > 1 && launch_merge(a, stream) != hipSuccess) return DDTV_EDEVICE;
     return DDTV_OK;
 }
 

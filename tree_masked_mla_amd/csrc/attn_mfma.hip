@@ -33,8 +33,8 @@
 //    where the cache stream is the bound): a workgroup owns 32 rows, and wave
 //    pairs 2k and 2k + 1 both own rows 16k .. 16k + 15 but take cache rows 0..15
 //    and 16..31 of every tile respectively, each with its own online softmax.
-//    The two halves leave two partials per split, combined by the merge pass like
-//    any other split.  With 16 rows this puts pairs 0 and 1 (waves 0..3, one per
+//    The two halves are combined inside the workgroup at the end (through LDS),
+//    so a split leaves one partial like the usual mode.  With 16 rows this puts pairs 0 and 1 (waves 0..3, one per
 //    SIMD) to work where otherwise one pair (two SIMDs) would do all the matrix
 //    work of the tile; the idle waves 4..7 then issue every tile load, and the
 //    score-swap barrier waits for LDS work only, so the next tile streams in
@@ -380,6 +380,49 @@ __device__ __forceinline__ void swap_barrier() {
         __syncthreads();
 }
 
+// Row-half mode: pairs 2k and 2k + 1 hold the same 16 query rows, each with its
+// own online softmax over one half of every tile.  Pair 2k + 1 hands its running
+// max, sums and weighted sums to pair 2k through LDS (the tile buffers are free
+// once every wave has left the loop), and pair 2k folds them into its own with
+// the log-sum-exp combination the split merge uses.  So a split leaves one
+// partial, and a batch row with a single split gets its output here.
+template <int HALF>
+__device__ __forceinline__ void combine_halves(Smem& sm, f32x4 (&oacc)[16], float& m_run, float& l_lane, int wave,
+                                               int lane) {
+    const int pair = wave >> 1, slot = (pair >> 1) * 2 + HALF, rh = pair & 1;
+    f32x4* xo = &sm.kv[0][0] + slot * 16 * 64;                           // 16 KiB per slot
+    float2* xml = reinterpret_cast<float2*>(&sm.kv[1][0]) + slot * 64;
+    __syncthreads();   // every wave is done with the tile buffers
+    if (rh) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) xo[c * 64 + lane] = oacc[c];
+        xml[lane] = make_float2(m_run, l_lane);
+    }
+    __syncthreads();
+    if (!rh) {
+        // lane (g, n): statistics of row n; accumulators of rows 4g + j
+        const float2 pm = xml[lane];
+        const float M = fmaxf(m_run, pm.x);
+        const float a0 = (m_run == -INFINITY) ? 0.f : exp2f(m_run - M);   // an empty half weighs 0
+        const float a1 = (pm.x == -INFINITY) ? 0.f : exp2f(pm.x - M);
+        l_lane = a0 * l_lane + a1 * pm.y;
+        m_run = M;
+        const int g = lane >> 4;
+        float w0[4], w1[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            w0[j] = __shfl(a0, 4 * g + j, 64);
+            w1[j] = __shfl(a1, 4 * g + j, 64);
+        }
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const f32x4 x = xo[c * 64 + lane];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) oacc[c][j] = w0[j] * oacc[c][j] + w1[j] * x[j];
+        }
+    }
+}
+
 // One workgroup's work; HALF is the wave's half of the pair (wave-uniform);
 // kHv selects row-half mode.
 template <int KV, int HALF, bool kHv>
@@ -471,6 +514,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
             swap_barrier<kHv>();
             if (KV != DDTV_F32 && more) store_tile_narrow<KV>(sm.kv[(it + 1) & 1], stage, tid);
         }
+        if constexpr (kHv) combine_halves<HALF>(sm, oacc, m_run, l_lane, wave, lane);   // (its barriers)
         return;   // no rows to write
     }
     for (int it = 0; it < ntiles; ++it) {
@@ -502,12 +546,17 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
                               P, kv_hi, rh);
     }
 
+    if constexpr (kHv) {
+        combine_halves<HALF>(sm, oacc, m_run, l_lane, wave, lane);
+        if (rh) return;   // pair 2k writes the combined rows
+    }
+
     // ---- epilogue: output rows pair*16 + 4g + j of the tile, dims 256*HALF + 64T + 4n + (0..3)
     float l_row = l_lane + wave_xor(l_lane, 16);
     l_row += wave_xor(l_row, 32);
     const float kLn2 = 0.69314718055994530942f;
     const int orow_base = rt * kRowsWG + rgrp * 16 + 4 * g;
-    if (!kHv && n_b == 1) {
+    if (n_b == 1) {
         const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -524,9 +573,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         if (HALF == 0 && a.lse && g == 0 && row_ok)
             a.lse[(int64_t)b * a.R + myrow] = l_row > 0.f ? (m_run + log2f(l_row)) * kLn2 : -INFINITY;
     } else {
-        // partial entry of this split (row-half mode: two per split, one per half)
-        const int64_t pbase = kHv ? ((int64_t)b * 2 * a.n_split + 2 * s + rh) * a.R
-                                  : ((int64_t)b * a.n_split + s) * a.R;
+        // partial entry of this split
+        const int64_t pbase = ((int64_t)b * a.n_split + s) * a.R;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int orow = orow_base + j;

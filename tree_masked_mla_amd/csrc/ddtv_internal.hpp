@@ -30,14 +30,14 @@ struct AttnArgs {
     const int32_t* order;    // [B] batch row of each grid slot, or null for the identity
     float* out;              // [B][Q][H][512]
     float* lse;              // [B][Q][H] or null
-    float* part_o;           // [B][n_split * (1 + halves)][R][512]   (n_split > 1 or halves)
-    float2* part_ml;         // [B][n_split * (1 + halves)][R]  {m (log2 units), l}
+    float* part_o;           // [B][n_split][R][512]   (n_split > 1)
+    float2* part_ml;         // [B][n_split][R]  {m (log2 units), l}
     int B, Q, H, W, R;       // R = Q*H query rows per batch row
     int n_rt;                // row tiles per batch row
     int split_len;           // KV positions per split (multiple of kSplitQuantum)
     int n_split;             // splits per batch row in the grid (max over rows)
     int spread;              // 1: work item = workgroup id; 0: XCD-local order (xcd_remap)
-    int halves;              // 1: row-half mode (32 rows per workgroup, 2 partials per split; matrix kernel)
+    int halves;              // 1: row-half mode (32 rows per workgroup, halves combined in it; matrix kernel)
     float scale_log2;        // scale * log2(e)
 };
 

@@ -10,8 +10,7 @@
 //
 // 128 threads per query row and partial group (one float4 of the 512-d output
 // each).  Rows whose batch row needed a single split were finished by the
-// attention kernel and are skipped (except in row-half mode, where every split
-// leaves two partials).  The splits are read in batches of kBatch independent
+// attention kernel and are skipped.  The splits are read in batches of kBatch independent
 // loads and folded in with an online rescale (the running maximum moves batch by
 // batch), so up to kBatch splits cost one memory round trip.  With many partials
 // and few rows (decode shapes) G groups of 128 threads share a row, each taking
@@ -37,11 +36,10 @@ __global__ __launch_bounds__(G == 1 ? 256 : 128 * G) void merge_kernel(AttnArgs 
     const int b = (int)(gr / a.R);
     const int row = (int)(gr - (int64_t)b * a.R);
     const int kv_len = a.rows[b].kv_len;
-    const int hm = a.halves ? 2 : 1;                   // partials per split
-    const int n_b = hm * ((kv_len + a.split_len - 1) / a.split_len);
+    const int n_b = (kv_len + a.split_len - 1) / a.split_len;   // this batch row's partials
     if (n_b <= 1) return;
     const int c = threadIdx.x & 127;
-    const int64_t pbase = (int64_t)b * hm * a.n_split * a.R + row;   // partial s at pbase + s * R
+    const int64_t pbase = (int64_t)b * a.n_split * a.R + row;   // partial s at pbase + s * R
     const float4* po = reinterpret_cast<const float4*>(a.part_o);
     // this group's partials: [s_lo, s_hi)
     const int per = (n_b + G - 1) / G;
@@ -120,7 +118,7 @@ hipError_t launch_merge(const AttnArgs& a, hipStream_t stream) {
     const int64_t rows = (int64_t)a.B * a.R;
     // Partial groups per row: enough that each group's share is one batch of
     // loads, used only while the rows alone leave most CUs without a workgroup.
-    const int n_part = (a.halves ? 2 : 1) * a.n_split;
+    const int n_part = a.n_split;
     int G = 1;
     while (G < 8 && n_part > G * kBatch && rows * G < 2048) G *= 2;
     switch (G) {
