@@ -214,7 +214,10 @@ typedef enum {
 /* Optional controls for ddtv_verify_attn_ex (zero-initialise for defaults). */
 typedef struct {
     int32_t path;          /* ddtv_path */
-    int32_t split_len;     /* KV positions per split; 0 = automatic; else a multiple of 32 */
+    int32_t split_len;     /* KV positions per split; 0 = automatic; else a multiple of 16 (cache
+                              tiles hold 32 rows; the fp32 matrix kernel on an fp32 cache runs a
+                              split's last tile of at most 16 rows as half a tile, the other
+                              kernels mask the unused rows of a whole one) */
     hipEvent_t attn_begin; /* if non-NULL: recorded on `stream` right before the main kernel */
     hipEvent_t attn_end;   /* if non-NULL: recorded on `stream` right after it (before the merge) */
     int32_t wg_order;      /* ddtv_wg_order */

@@ -115,7 +115,7 @@ def test_verify_host_errors(lib):
     assert verify_call(lib, vis, scale=float("inf")) == E
     assert verify_call(lib, vis, kv_dtype=3) == U        # FP8 E4M3 (2) is the last cache dtype
     assert verify_call(lib, vis, opts=dd.make_opts(path=4)) == U
-    assert verify_call(lib, vis, opts=dd.make_opts(split_len=100)) == E   # not a multiple of 32
+    assert verify_call(lib, vis, opts=dd.make_opts(split_len=100)) == E   # not a multiple of 16
     assert verify_call(lib, vis, opts=dd.make_opts(split_len=-64)) == E
     assert verify_call(lib, vis, opts=dd.make_opts(wg_order=3)) == U
     bad = fake_vis()
@@ -455,15 +455,15 @@ def workload_vis(name, q_len=None):
 
 
 @pytest.mark.parametrize("name,q_len,dtype,want", [
-    ("c3", None, 0, (2, 288, 15, 240, dd.DDTV_ORDER_XCD_LOCAL)),
+    ("c3", None, 0, (2, 272, 16, 256, dd.DDTV_ORDER_XCD_LOCAL)),
     ("c4", None, 0, (2, 32896, 1, 256, dd.DDTV_ORDER_XCD_LOCAL)),
     ("c4", 1, 0, (2, 1056, 32, 256, dd.DDTV_ORDER_XCD_LOCAL)),
     ("c5", None, 1, (2, None, 1, 2048, dd.DDTV_ORDER_SPREAD)),
 ])
 def test_plans_of_the_benchmarked_workloads(lib, name, q_len, dtype, want):
-    """The split plans the measurements were taken with: c3 in 15 splits on 240
-    workgroups, c4 unsplit, c4 sizes at q_len 1 in 32 splits (row-half mode),
-    c5 unsplit in the spread order."""
+    """The split plans the measurements were taken with: c3 in 16 splits of 272
+    rows (the last tile of each a half tile) on 256 workgroups, c4 unsplit, c4
+    sizes at q_len 1 in 32 splits (row-half mode), c5 unsplit in the spread order."""
     vis, H = workload_vis(name, q_len)
     rc, path, split_len, n_split, wgs, order = dd.ddtv_plan_info(vis, H, dtype)
     assert rc == dd.DDTV_OK
@@ -491,3 +491,20 @@ def test_uncached_planning_is_cheap(lib, name, q_len, dtype):
     med = statistics.median(ts)
     print(f"{name} q_len {q_len or vis0.vis.Q}: uncached plan {med * 1e6:.1f} us")
     assert med < 200e-6, f"{name}: uncached planning took {med * 1e6:.0f} us"
+
+
+def test_split_lengths_off_the_tile_grid(lib):
+    """Split lengths are multiples of 16; the planner takes one off the 32-row grid
+    (an odd multiple of 16) only for the fp32 matrix kernel on an fp32 cache, whose
+    last tile of at most 16 rows then runs as half a tile, and only when the grid
+    starts in one round (c3's shape: 16 splits of 272 rows on 256 workgroups)."""
+    vis = fake_vis(B=1, Q=64, prefix=(4096,))
+    assert verify_call(lib, vis, opts=dd.make_opts(split_len=40)) == dd.DDTV_EINVAL
+    rc, path, L, ns, wg, order = dd.ddtv_plan_info(vis, 16, 0, dd.make_opts(split_len=48))
+    assert rc == 0 and (L, ns) == (48, (4160 + 47) // 48)
+    rc, path, L, ns, wg, order = dd.ddtv_plan_info(vis, 16, 0)   # (256 CUs: MI355X, or no device)
+    assert rc == 0 and (L, ns, wg) == (272, 16, 256), (L, ns, wg)
+    # the other kernels keep 32-row split lengths: bf16 matrix kernel, FP8 cache, vector path
+    for dtype, opts in [(dd.DDTV_BF16, None), (dd.DDTV_FP8_E4M3, None), (0, dd.make_opts(path=dd.DDTV_PATH_VALU))]:
+        rc, path, L, ns, wg, order = dd.ddtv_plan_info(vis, 16, dtype, opts)
+        assert rc == 0 and L % 32 == 0, (dtype, L)

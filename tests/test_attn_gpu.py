@@ -61,7 +61,10 @@ def test_c2_chain_is_causal(path):
 
 
 def test_c3_full():
-    check_full(wl.config("c3"))
+    """c3 in the benchmark's plan: 16 splits of 272 rows (8.5 tiles each, the last
+    one a half tile) on 256 workgroups; every row against the oracle."""
+    r, _, _ = check_full(wl.config("c3"))
+    assert r.plan()[2] % 32 == 16, r.plan()
 
 
 # ----------------------------------------------------------------------------- reduced dense shapes
@@ -118,6 +121,27 @@ def test_split_count_invariance():
         outs.append(out)
     for o in outs[1:]:
         assert np.abs(o - outs[0]).max() < 1e-5
+
+
+# Split lengths that are odd multiples of 16: every split ends mid-tile.  The fp32
+# matrix kernel on an fp32 cache runs such a last tile as half a tile (one score
+# block, half of P.V); the other kernels mask the unused rows of a whole tile.
+@pytest.mark.parametrize("kv_dtype,path,B,H,Q,prefix,split_len", [
+    (wl.F32, 2, 2, 16, 64, [600, 300], 112),   # 64-row workgroups, tree rows inside half tiles
+    (wl.F32, 2, 1, 8, 9, [40], 48),            # tree nodes 0..7 in split 0's half tile, node 8 alone in split 1
+    (wl.F32, 2, 1, 8, 9, [0], 16),             # one split of one half tile (the tree only)
+    (wl.F32, 2, 3, 8, 5, [77, 0, 30], 80),     # 40 rows, ragged batch rows, a row with no prefix
+    (wl.F32, 1, 2, 8, 9, [100, 37], 48),       # vector path
+    (wl.F32, 2, 2, 16, 1, [1000, 3], 48),      # row-half mode (16 rows)
+    (wl.BF16, 2, 2, 16, 64, [600, 300], 112),  # bf16 matrix kernel
+    (wl.FP8, 2, 2, 16, 64, [600, 300], 112),   # FP8 cache on the fp32 matrix kernel (whole tiles)
+])
+def test_half_tile_splits(kv_dtype, path, B, H, Q, prefix, split_len):
+    w = wl.make_workload(f"halftile{B}x{H}x{Q}", 8100 + B * 100 + H * 10 + Q, B=B, H=H, Q=Q, prefix=prefix,
+                         tree="uniform", kv_dtype=kv_dtype)
+    r, _, _ = check_full(w, path=path, split_len=split_len,
+                         what=f"half tiles B{B} H{H} Q{Q} P{prefix} dtype {kv_dtype} split {split_len}")
+    assert r.plan()[2] == split_len
 
 
 # Many partials on few rows: the merge shares a row's partials among 2, 4 or 8

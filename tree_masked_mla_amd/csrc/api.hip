@@ -154,21 +154,31 @@ struct XcdSchedule {
 };
 
 constexpr double kExitCost = 0.02;   // a work item past its row's last split: starts and exits
+constexpr double kHalfTileCost = 0.65;  // a last tile of at most 16 rows on the fp32 matrix kernel (measured)
+
+// Tile-times of a split of len cache rows: one per 32-row tile; with half tiles
+// (fp32 matrix kernel, fp32 cache, usual mode) a last tile of at most 16 rows
+// costs kHalfTileCost.
+double tiles_of(int len, bool half) {
+    const int full = len / kTile, r = len % kTile;
+    return (double)full + (r == 0 ? 0.0 : (half && r <= kTile / 2) ? kHalfTileCost : 1.0);
+}
 
 // Total work of the grid spread evenly over all CUs, plus the merge pass: a
 // lower bound on the makespan, and one that grows with the split count (each
 // split adds its set-up and merge traffic).
 double fluid_bound(const std::vector<int>& kv, int n_rt, int L, int cus, double setup_tiles,
-                   double merge_tiles_per_partial_row_split, int64_t R) {
+                   double merge_tiles_per_partial_row_split, int64_t R, bool half) {
     int n_split = 1;
     for (int k : kv) n_split = std::max(n_split, (k + L - 1) / L);
-    const int full_tiles = (L + kTile - 1) / kTile;
+    half = half && L % kTile != 0;   // (the kernel's half-tile variant runs only then)
+    const double full_tiles = tiles_of(L, half);
     double work = 0.0, merge = 0.0;
     for (int k : kv) {
         const int nb = (k + L - 1) / L;
         const int last = k - (nb - 1) * L;
         work += (double)n_rt * ((double)(nb - 1) * (setup_tiles + full_tiles) + setup_tiles +
-                                (double)((last + kTile - 1) / kTile) + (double)(n_split - nb) * kExitCost);
+                                tiles_of(last, half) + (double)(n_split - nb) * kExitCost);
         if (nb > 1) merge += merge_tiles_per_partial_row_split * (double)nb * (double)R;
     }
     return work / cus + merge;
@@ -185,12 +195,13 @@ double fluid_bound(const std::vector<int>& kv, int n_rt, int L, int cus, double 
 // simulated run by run.  `bound`: give up (returning at least bound) once the
 // total work alone shows the plan cannot beat it.
 double estimate(const std::vector<int>& kv, int n_rt, int L, int cus, double setup_tiles,
-                double merge_tiles_per_partial_row_split, int64_t R, bool spread,
+                double merge_tiles_per_partial_row_split, int64_t R, bool half, bool spread,
                 double bound = 1e300) {
     const int per_xcd = std::max(1, std::min(kMaxCusPerXcd, cus / kXcds));
     int n_split = 1;
     for (int k : kv) n_split = std::max(n_split, (k + L - 1) / L);
     const int64_t G = (int64_t)kv.size() * n_split * n_rt;
+    half = half && L % kTile != 0;   // (the kernel's half-tile variant runs only then)
     double merge = 0.0;   // each partial row is written, then read by the merge pass
     for (int k : kv) {
         const int parts = (k + L - 1) / L;
@@ -198,15 +209,15 @@ double estimate(const std::vector<int>& kv, int n_rt, int L, int cus, double set
     }
     auto cost = [&](int b, int s) {
         const int len = std::min(L, kv[b] - s * L);
-        return len > 0 ? setup_tiles + (double)((len + kTile - 1) / kTile) : kExitCost;
+        return len > 0 ? setup_tiles + tiles_of(len, half) : kExitCost;
     };
     const double fluid =
-        fluid_bound(kv, n_rt, L, cus, setup_tiles, merge_tiles_per_partial_row_split, R);
+        fluid_bound(kv, n_rt, L, cus, setup_tiles, merge_tiles_per_partial_row_split, R, half);
     if (fluid >= bound) return fluid;
     if (G <= (int64_t)per_xcd * kXcds) {   // no XCD gets more items than CUs: all start at once
         int longest = 0;
         for (int k : kv) longest = std::max(longest, std::min(L, k));
-        return setup_tiles + (double)((longest + kTile - 1) / kTile) + merge;
+        return setup_tiles + tiles_of(longest, half) + merge;
     }
     if ((int64_t)kv.size() * n_split * kXcds > ((int64_t)1 << 20)) return fluid;   // thousands per CU even out
     XcdSchedule X;
@@ -362,7 +373,7 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     if (R > (int64_t)INT32_MAX / 2) return DDTV_EUNSUPPORTED;
     p->n_rt = (int)((R + p->rows_per_wg - 1) / p->rows_per_wg);
     const int max_kv = vis->max_kv;
-    const int single = (int)round_up((size_t)max_kv, kSplitQuantum);
+    const int single = (int)round_up((size_t)max_kv, kTile);
 
     std::vector<int> kv(vis->B), kv_sorted(vis->B);
     for (int b = 0; b < vis->B; ++b) kv[b] = vis->prefix_host ? vis->prefix_host[b] + vis->Q : max_kv;
@@ -375,13 +386,21 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     }
     const int cus = cu_count();
     // Tile-time units: one 32-row cache tile through one workgroup.  A partial
-    // row costs 2 x 2 KiB of traffic in the merge (written, then read).
+    // row costs 2 x 2 KiB of traffic in the merge (written, then read); for the
+    // fp32 matrix kernel the write is counted in its set-up (it ends the
+    // workgroup), which leaves the 2 KiB the merge pass reads (measured on the
+    // 15-split, 1024-row plan: 7.8 us for 31.5 MB).
     // tile_us: rough time of one tile through one workgroup (fp32 MFMA and bf16
     // MFMA: 64 rows; VALU: 16 rows)
     const bool mfma = p->path != DDTV_PATH_VALU;
+    // The fp32 matrix kernel on an fp32 cache (usual mode) runs a split's last tile
+    // of at most 16 rows as half a tile (when the split length is an odd multiple
+    // of 16), so split lengths 16 rows off the tile grid are candidates too; the
+    // other kernels pay a whole tile for such a tile.
+    const bool half = mfma && !p->bf16_mma && !p->halves && kv_dtype == DDTV_F32;
     const double setup = mfma ? 2.0 : 1.0;
     const double tile_us = p->bf16_mma ? 0.9 : (mfma ? 7.3 : 1.0);
-    const double merge_per_row_split = (4096.0 / 4.0e12) * 1e6 / tile_us;   // ~4 TB/s effective
+    const double merge_per_row_split = ((half ? 2048.0 : 4096.0) / 4.0e12) * 1e6 / tile_us;   // ~4 TB/s effective
     // Simulated makespan at split length L under the requested order, or under the
     // better of the two.  The XCD-local order lets every query tile that reads a
     // cache tile find it in its XCD's L2, so the spread order has to be clearly
@@ -391,11 +410,11 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
         if (order_req != DDTV_ORDER_AUTO) {
             *order = order_req;
             return order_req == DDTV_ORDER_SPREAD
-                       ? estimate(kv_sorted, p->n_rt, L, cus, setup, merge_per_row_split, R, true, bound)
-                       : estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, false, bound);
+                       ? estimate(kv_sorted, p->n_rt, L, cus, setup, merge_per_row_split, R, half, true, bound)
+                       : estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, half, false, bound);
         }
-        const double local = estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, false, bound);
-        const double spread = estimate(kv_sorted, p->n_rt, L, cus, setup, merge_per_row_split, R, true,
+        const double local = estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, half, false, bound);
+        const double spread = estimate(kv_sorted, p->n_rt, L, cus, setup, merge_per_row_split, R, half, true,
                                        std::min(bound, local * 0.98));
         *order = spread < local * 0.98 ? DDTV_ORDER_SPREAD : DDTV_ORDER_XCD_LOCAL;
         return std::min(local, spread);
@@ -413,8 +432,27 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
         int prevL = 0, worse = 0;
         // (every S below 32, then steps of S / 32: the split lengths grow dense)
         for (int S = 1;; S += S < 32 ? 1 : S / 32) {
-            const int L = (int)round_up((size_t)((max_kv + S - 1) / S), kSplitQuantum);
+            const int L = (int)round_up((size_t)((max_kv + S - 1) / S), kTile);
             if (L < 4 * kTile && S > 1) break;
+            // With half tiles, the length 16 rows shorter is a candidate too when its
+            // grid starts in one round (there the estimate is the longest work item;
+            // the simulation of later rounds is not accurate enough to choose by
+            // fractions of a tile).
+            if (half) {
+                const int Lh = (int)round_up((size_t)((max_kv + S - 1) / S), kSplitQuantum);
+                int64_t wh = 0;
+                for (int b = 0; b < vis->B; ++b) wh += (int64_t)((kv[b] + Lh - 1) / Lh) * p->n_rt;
+                if (Lh != L && wh <= cus && (S == 1 || partial_bytes(vis->B, R, (max_kv + Lh - 1) / Lh) <= ws_cap)) {
+                    int order = DDTV_ORDER_XCD_LOCAL;
+                    const double e = cost_at(Lh, &order, best * 0.98);
+                    if (e < best * 0.98) {
+                        best = e;
+                        bestL = Lh;
+                        bestOrder = order;
+                        worse = 0;
+                    }
+                }
+            }
             if (L == prevL) continue;
             prevL = L;
             int64_t wgs = 0;
@@ -422,7 +460,7 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
             if (wgs > wg_cap && S > 1) break;
             const int parts_L = (max_kv + L - 1) / L;
             if (S > 1 && partial_bytes(vis->B, R, parts_L) > ws_cap) break;   // more splits only need more
-            if (S > 1 && fluid_bound(kv, p->n_rt, L, cus, setup, merge_per_row_split, R) >= best * 0.98)
+            if (S > 1 && fluid_bound(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, half) >= best * 0.98)
                 break;   // its lower bound cannot beat the best by 2 %, nor can more splits'
             int order = DDTV_ORDER_XCD_LOCAL;
             const double e = cost_at(L, &order, best * 0.98);   // a plan must beat the best by 2 %

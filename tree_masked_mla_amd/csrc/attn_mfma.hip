@@ -425,7 +425,7 @@ __device__ __forceinline__ void combine_halves(Smem& sm, f32x4 (&oacc)[16], floa
 
 // One workgroup's work; HALF is the wave's half of the pair (wave-uniform);
 // kHv selects row-half mode.
-template <int KV, int HALF, bool kHv>
+template <int KV, int HALF, bool kHv, bool kHalfLast>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, int s, int rt, int wave,
                                           int lane) {
     const int tid = wave * 64 + lane;
@@ -517,7 +517,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         if constexpr (kHv) combine_halves<HALF>(sm, oacc, m_run, l_lane, wave, lane);   // (its barriers)
         return;   // no rows to write
     }
-    for (int it = 0; it < ntiles; ++it) {
+    // kHalfLast: a last tile with at most 16 rows (a split that ends mid-tile, or
+    // a short end of the cache) runs as half a tile -- one score block and half of
+    // P.V; the other half would only add zeros.  (Its own instantiation, so the
+    // loop of the other kernels is compiled exactly as before.)
+    const int t_last = kv_lo + (ntiles - 1) * kTile;
+    const int nloop = (kHalfLast && kv_hi - t_last <= kTile / 2) ? ntiles - 1 : ntiles;
+    for (int it = 0; it < nloop; ++it) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();                                  // tile `it` is in LDS
         const bool more = it + 1 < ntiles;
@@ -544,6 +550,17 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
         swap_barrier<kHv || early_issue>();               // partner's partial scores are in LDS
         sm_pv_slot<HALF, kHv, KV != DDTV_BF16>(oacc, sx_mine, sx_partner, Kb, to, m_run, l_lane, mrow, g, n, lane, kv_lo + it * kTile,
                               P, kv_hi, rh);
+    }
+    if constexpr (kHalfLast) {
+        if (nloop < ntiles) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();                              // the last tile is in LDS
+            const char* Kb = reinterpret_cast<const char*>(sm.kv[nloop & 1]);
+            qk_slot<HALF, true>(Kb, to, qreg, sx_mine, lane, [] {}, 0);
+            swap_barrier<early_issue>();
+            sm_pv_slot<HALF, true, KV != DDTV_BF16>(oacc, sx_mine, sx_partner, Kb, to, m_run, l_lane, mrow, g, n,
+                                                    lane, t_last, P, kv_hi, 0);
+        }
     }
 
     if constexpr (kHv) {
@@ -591,7 +608,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
 }
 
 // kHv: row-half mode (its own kernel, so the code of the usual mode is unchanged).
-template <int KV, bool kHv>
+template <int KV, bool kHv, bool kHalfLast>
 __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs a) {
     __shared__ Smem sm;
     const int64_t w = work_item(a);
@@ -603,17 +620,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (wave & 1)
-        attn_body<KV, 1, kHv>(a, sm, b, s, rt, wave, lane);
+        attn_body<KV, 1, kHv, kHalfLast>(a, sm, b, s, rt, wave, lane);
     else
-        attn_body<KV, 0, kHv>(a, sm, b, s, rt, wave, lane);
+        attn_body<KV, 0, kHv, kHalfLast>(a, sm, b, s, rt, wave, lane);
 }
 
 template <int KV>
 void launch_kv(const AttnArgs& a, int64_t grid, hipStream_t stream) {
     if (a.halves)
-        hipLaunchKernelGGL((attn_mfma_kernel<KV, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((attn_mfma_kernel<KV, true, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    else if (KV == DDTV_F32 && a.split_len % kTile != 0)   // splits end mid-tile: half last tiles
+        hipLaunchKernelGGL((attn_mfma_kernel<KV, false, KV == DDTV_F32>), dim3((unsigned)grid), dim3(kThreads), 0,
+                           stream, a);
     else
-        hipLaunchKernelGGL((attn_mfma_kernel<KV, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((attn_mfma_kernel<KV, false, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
 }
 
 }  // namespace

@@ -15,7 +15,7 @@ constexpr int kDQK = kDLat + kDRope;      // 576
 constexpr int kMaxQ = DDTV_MAX_Q;         // 256
 constexpr int kMaxW = kMaxQ / 32;         // 8 mask words
 constexpr int kTile = 32;                 // KV positions per LDS tile (both kernels)
-constexpr int kSplitQuantum = kTile;      // split lengths are multiples of the tile
+constexpr int kSplitQuantum = kTile / 2;  // split lengths are multiples of half a tile
 constexpr int kVisChunk = 64;             // batch rows described per visibility launch
 constexpr int kXcds = 8;                  // MI355X: 8 XCDs, workgroups dealt round-robin
 
