@@ -504,6 +504,13 @@ def test_split_lengths_off_the_tile_grid(lib):
     assert rc == 0 and (L, ns) == (48, (4160 + 47) // 48)
     rc, path, L, ns, wg, order = dd.ddtv_plan_info(vis, 16, 0)   # (256 CUs: MI355X, or no device)
     assert rc == 0 and (L, ns, wg) == (272, 16, 256), (L, ns, wg)
+    # a half tile has to beat the tile-aligned length by the planner's 2 % margin: a c4-sized
+    # batch whose longest prefix grew by 5 rows keeps one tile-aligned split
+    grown = fake_vis(B=8, Q=128, prefix=(32768 + 5,) + (32768,) * 7)
+    rc, path, L, ns, wg, order = dd.ddtv_plan_info(grown, 16, 0)
+    assert rc == 0 and (L, ns) == (32928, 1), (L, ns)
+    small = fake_vis(B=1, Q=64, prefix=(1000,))           # 3.5 tiles beat 4 by more than that
+    assert dd.ddtv_plan_info(small, 16, 0)[2:4] == (112, 10)
     # the other kernels keep 32-row split lengths: bf16 matrix kernel, FP8 cache, vector path
     for dtype, opts in [(dd.DDTV_BF16, None), (dd.DDTV_FP8_E4M3, None), (0, dd.make_opts(path=dd.DDTV_PATH_VALU))]:
         rc, path, L, ns, wg, order = dd.ddtv_plan_info(vis, 16, dtype, opts)

@@ -429,31 +429,37 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
         const int64_t wg_cap = (int64_t)cus * 64;
         // Candidates: the longest row cut into S equal tile-aligned pieces, S = 1, 2, ...
         // (stop once the grid is far beyond the device or pieces get short).
+        // With half tiles, the length 16 rows shorter than a tile-aligned candidate
+        // is a candidate too, after it (so it has to beat it by 2 %), when its grid
+        // starts in one round: there the estimate is the longest work item, while
+        // the simulation of later rounds is not accurate enough to choose by
+        // fractions of a tile.
+        int prevLh = 0;
+        auto try_half = [&](int S, int L) {
+            if (!half) return;
+            const int Lh = (int)round_up((size_t)((max_kv + S - 1) / S), kSplitQuantum);
+            if (Lh == L || Lh == prevLh) return;
+            prevLh = Lh;
+            int64_t wh = 0;
+            for (int b = 0; b < vis->B; ++b) wh += (int64_t)((kv[b] + Lh - 1) / Lh) * p->n_rt;
+            if (wh > cus || (S > 1 && partial_bytes(vis->B, R, (max_kv + Lh - 1) / Lh) > ws_cap)) return;
+            int order = DDTV_ORDER_XCD_LOCAL;
+            const double e = cost_at(Lh, &order, best * 0.98);
+            if (e < best * 0.98) {
+                best = e;
+                bestL = Lh;
+                bestOrder = order;
+            }
+        };
         int prevL = 0, worse = 0;
         // (every S below 32, then steps of S / 32: the split lengths grow dense)
         for (int S = 1;; S += S < 32 ? 1 : S / 32) {
             const int L = (int)round_up((size_t)((max_kv + S - 1) / S), kTile);
             if (L < 4 * kTile && S > 1) break;
-            // With half tiles, the length 16 rows shorter is a candidate too when its
-            // grid starts in one round (there the estimate is the longest work item;
-            // the simulation of later rounds is not accurate enough to choose by
-            // fractions of a tile).
-            if (half) {
-                const int Lh = (int)round_up((size_t)((max_kv + S - 1) / S), kSplitQuantum);
-                int64_t wh = 0;
-                for (int b = 0; b < vis->B; ++b) wh += (int64_t)((kv[b] + Lh - 1) / Lh) * p->n_rt;
-                if (Lh != L && wh <= cus && (S == 1 || partial_bytes(vis->B, R, (max_kv + Lh - 1) / Lh) <= ws_cap)) {
-                    int order = DDTV_ORDER_XCD_LOCAL;
-                    const double e = cost_at(Lh, &order, best * 0.98);
-                    if (e < best * 0.98) {
-                        best = e;
-                        bestL = Lh;
-                        bestOrder = order;
-                        worse = 0;
-                    }
-                }
+            if (L == prevL) {
+                try_half(S, L);
+                continue;
             }
-            if (L == prevL) continue;
             prevL = L;
             int64_t wgs = 0;
             for (int b = 0; b < vis->B; ++b) wgs += (int64_t)((kv[b] + L - 1) / L) * p->n_rt;
@@ -472,6 +478,7 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
             } else if (wgs > 2 * (int64_t)cus && ++worse >= 8) {
                 break;               // past a full device and no longer improving
             }
+            try_half(S, L);
             if (S >= 4096) break;
         }
         p->split_len = bestL;
