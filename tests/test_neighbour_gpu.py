@@ -108,8 +108,9 @@ def test_prepare_query_full_size_sampled(name):
     assert np.isfinite(qa).all() and np.isfinite(qr).all()
 
 
+# (the small grids run the split-K kernel; (640, 4, 128) the narrow one, (1024, 16, 128) the wide one)
 @pytest.mark.parametrize("M,H,d_v", [(9, 8, 128), (111, 5, 96), (64, 3, 32), (1, 1, 1), (1024, 16, 128),
-                                     (200, 2, 512)])
+                                     (200, 2, 512), (640, 4, 128)])
 def test_value_proj_matches_oracle(M, H, d_v):
     import tree_masked_mla_amd as dd
     say(f"value_proj M={M} H={H} d_v={d_v}")

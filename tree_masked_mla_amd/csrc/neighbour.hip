@@ -77,9 +77,9 @@ struct Stage {
 };
 
 template <bool kBTrans, bool kWide>
-__device__ __forceinline__ void load_stage(const ProjArgs& p, int h, int m0, int n0, int k0, Stage<kWide>& s) {
+__device__ __forceinline__ void load_stage(const ProjArgs& p, int h, int m0, int n0, int k0, Stage<kWide>& s,
+                                           int t) {
     using G = Geo<kWide>;
-    const int t = threadIdx.x;
 #pragma unroll
     for (int r = 0; r < G::ALoads; ++r) {
         const int idx = t + r * G::Threads;
@@ -103,9 +103,8 @@ __device__ __forceinline__ void load_stage(const ProjArgs& p, int h, int m0, int
 }
 
 template <bool kBTrans, bool kWide>
-__device__ __forceinline__ void store_stage(float* As, float* Bs, const Stage<kWide>& s) {
+__device__ __forceinline__ void store_stage(float* As, float* Bs, const Stage<kWide>& s, int t) {
     using G = Geo<kWide>;
-    const int t = threadIdx.x;
 #pragma unroll
     for (int r = 0; r < G::ALoads; ++r) {
         const int idx = t + r * G::Threads;
@@ -190,13 +189,13 @@ __global__ __launch_bounds__(Geo<kWide>::Threads) void proj_gemm_kernel(ProjArgs
         for (int j = 0; j < 2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     Stage<kWide> st;
-    load_stage<kBTrans, kWide>(p, h, m0, n0, 0, st);
-    store_stage<kBTrans, kWide>(As[0], Bs[0], st);
+    load_stage<kBTrans, kWide>(p, h, m0, n0, 0, st, threadIdx.x);
+    store_stage<kBTrans, kWide>(As[0], Bs[0], st, threadIdx.x);
     __syncthreads();
     const int n_stage = p.K / kBK;
     for (int s = 0; s < n_stage; ++s) {
         const int cur = s & 1;
-        if (s + 1 < n_stage) load_stage<kBTrans, kWide>(p, h, m0, n0, (s + 1) * kBK, st);
+        if (s + 1 < n_stage) load_stage<kBTrans, kWide>(p, h, m0, n0, (s + 1) * kBK, st, threadIdx.x);
         const float* A = As[cur];
         const float* Bm = Bs[cur];
 #pragma unroll
@@ -215,7 +214,7 @@ __global__ __launch_bounds__(Geo<kWide>::Threads) void proj_gemm_kernel(ProjArgs
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
         }
         if (s + 1 < n_stage) {
-            store_stage<kBTrans, kWide>(As[cur ^ 1], Bs[cur ^ 1], st);
+            store_stage<kBTrans, kWide>(As[cur ^ 1], Bs[cur ^ 1], st, threadIdx.x);
             __syncthreads();
         }
     }
@@ -230,6 +229,107 @@ __global__ __launch_bounds__(Geo<kWide>::Threads) void proj_gemm_kernel(ProjArgs
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int n = n0 + wn + j * 16 + li;
+                if (n < p.N) c[n] = acc[i][j][r];
+            }
+        }
+    }
+}
+
+// Small grids with a long contraction (the value projection of a few tree nodes:
+// one 64-row tile and 4 column tiles per head, K = 512): four groups of 128
+// threads share one 64 x 32 output tile, group g taking the K stages g, g + 4,
+// ...; then groups 1..3 park their sums in LDS and group 0 adds them in group
+// order (deterministic) and writes C.  Four times the waves per workgroup and a
+// quarter of the stages each, where the narrow kernel ran 16 dependent stages on
+// 2 waves.
+constexpr int kSplitGroups = 4;
+
+template <bool kBTrans>
+__global__ __launch_bounds__(kSplitGroups * 128) void proj_gemm_splitk_kernel(ProjArgs p) {
+    using G = Geo<false>;
+    static_assert(G::Threads == 128 && G::WavesN == 1, "one narrow tile per group");
+    __shared__ float As[kSplitGroups][2][kAStage];
+    __shared__ float Bs[kSplitGroups][2][G::BStage];
+    const int h = blockIdx.z;
+    const int m0 = blockIdx.x * kBM, n0 = blockIdx.y * G::BN;
+    const int grp = threadIdx.x >> 7, t = threadIdx.x & 127;
+    const int lane = t & 63, wave = t >> 6;
+    const int wm = wave * 32;
+    const int li = lane & 15, lk = lane >> 4;
+
+    floatx4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int n_stage = p.K / kBK;
+    const int rounds = (n_stage + kSplitGroups - 1) / kSplitGroups;   // the same for every group
+    Stage<false> st;
+    if (grp < n_stage) {
+        load_stage<kBTrans, false>(p, h, m0, n0, grp * kBK, st, t);
+        store_stage<kBTrans, false>(As[grp][0], Bs[grp][0], st, t);
+    }
+    __syncthreads();
+    for (int r = 0; r < rounds; ++r) {
+        const int s = grp + r * kSplitGroups, sn = s + kSplitGroups;
+        const int cur = r & 1;
+        if (sn < n_stage) load_stage<kBTrans, false>(p, h, m0, n0, sn * kBK, st, t);
+        if (s < n_stage) {
+            const float* A = As[grp][cur];
+            const float* Bm = Bs[grp][cur];
+#pragma unroll
+            for (int kk = 0; kk < kBK; kk += 4) {
+                float a[2], b[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) a[i] = A[(wm + i * 16 + li) * kAStride + kk + lk];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    b[j] = kBTrans ? Bm[(j * 16 + li) * kBStrideNK + kk + lk] : Bm[(kk + lk) * G::BStrideKN + j * 16 + li];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+            }
+        }
+        if (r + 1 < rounds) {
+            if (sn < n_stage) store_stage<kBTrans, false>(As[grp][cur ^ 1], Bs[grp][cur ^ 1], st, t);
+            __syncthreads();
+        }
+    }
+    __syncthreads();   // every group is done with the stage buffers
+    float* park = &As[0][0][0];   // 3 groups x 16 values x 128 threads (24 KiB of the 36 KiB of A buffers)
+    static_assert((kSplitGroups - 1) * 16 * 128 <= kSplitGroups * 2 * kAStage, "parking fits the A buffers");
+    if (grp > 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) park[((grp - 1) * 16 + (i * 2 + j) * 4 + r) * 128 + t] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int g = 1; g < kSplitGroups; ++g)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][j][r] += park[((g - 1) * 16 + (i * 2 + j) * 4 + r) * 128 + t];
+    // D block (i, j): lane holds rows 4*lk + r, column li.
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t m = (int64_t)m0 + wm + i * 16 + 4 * lk + r;
+            if (m >= p.M) continue;
+            float* c = p.C + m * p.ldc + (int64_t)h * p.c_head;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int n = n0 + j * 16 + li;
                 if (n < p.N) c[n] = acc[i][j][r];
             }
         }
@@ -336,6 +436,15 @@ hipError_t launch_proj(const ProjArgs& p, bool b_trans, int cus, hipStream_t str
     const int64_t wide_wgs = (p.M + kBM - 1) / kBM * ((p.N + Geo<true>::BN - 1) / Geo<true>::BN) * p.H;
     const bool wide = wide_wgs >= cus;
     (void)hipGetLastError();   // report only this launch's error
+    // value projection of few rows: narrow tiles would still leave most CUs idle
+    // and run 16 dependent K stages each -- split K inside the workgroup instead
+    const int64_t narrow_wgs = (p.M + kBM - 1) / kBM * ((p.N + Geo<false>::BN - 1) / Geo<false>::BN) * p.H;
+    if (b_trans && !wide && 2 * narrow_wgs <= cus && p.K / kBK >= 2 * kSplitGroups) {
+        const dim3 grid((unsigned)((p.M + kBM - 1) / kBM), (unsigned)((p.N + Geo<false>::BN - 1) / Geo<false>::BN),
+                        (unsigned)p.H);
+        hipLaunchKernelGGL((proj_gemm_splitk_kernel<true>), grid, dim3(kSplitGroups * 128), 0, stream, p);
+        return hipGetLastError();
+    }
     if (b_trans)
         wide ? launch_proj_as<true, true>(p, stream) : launch_proj_as<true, false>(p, stream);
     else
