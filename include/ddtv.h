@@ -284,7 +284,7 @@ ddtv_status ddtv_verify_attn_ex(const float *q_abs, const float *q_rope, const v
  *   by the caller.  Each call writes every partial it reads, so nothing carries
  *   over from the previous call.
  */
-#define DDTV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+#define DDTV_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
 ddtv_status ddtv_verify_attn_noalloc(const float *q_abs, const float *q_rope, const void *ckv,
                                      const void *k_rope, ddtv_dtype kv_dtype, int32_t H,
                                      const ddtv_vis *vis, float scale, float *out, float *lse,

@@ -33,9 +33,9 @@ def _noalloc(r, opts=None):
 def test_noalloc_matches_workspace_entry_point_on_two_calls():
     import tree_masked_mla_amd as dd
     from tree_masked_mla_amd.runner import DeviceRun
-    big = wl.config("c3")                                   # 15 splits of 288: 30.1 MiB of partials
+    big = wl.config("c3")                                   # 16 splits of 272: 32.1 MiB of partials
     small = wl.make_workload("noalloc-small", 7301, B=3, H=8, Q=20, prefix=[300, 37, 0], tree="uniform")
-    cases = [(big, dd.make_opts(split_len=288)), (small, dd.make_opts(split_len=64))]
+    cases = [(big, dd.make_opts()), (small, dd.make_opts(split_len=64))]
     runs = []
     for w, opts in cases:
         r = DeviceRun(w, split_len=opts.split_len)

@@ -23,7 +23,7 @@ DDTV_F32, DDTV_BF16, DDTV_FP8_E4M3 = 0, 1, 2
 DDTV_PATH_AUTO, DDTV_PATH_VALU, DDTV_PATH_MFMA, DDTV_PATH_MFMA_F32 = 0, 1, 2, 3
 DDTV_ORDER_AUTO, DDTV_ORDER_XCD_LOCAL, DDTV_ORDER_SPREAD = 0, 1, 2
 D_LATENT, D_ROPE, MAX_Q = 512, 64, 256
-NOALLOC_SCRATCH_BYTES = 32 << 20   # DDTV_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 40 << 20   # DDTV_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = (
     "ddtv_vis_bytes", "ddtv_build_visibility", "ddtv_read_status", "ddtv_workspace_bytes",
