@@ -133,6 +133,8 @@ def test_split_count_invariance():
     (wl.F32, 2, 3, 8, 5, [77, 0, 30], 80),     # 40 rows, ragged batch rows, a row with no prefix
     (wl.F32, 1, 2, 8, 9, [100, 37], 48),       # vector path
     (wl.F32, 2, 2, 16, 1, [1000, 3], 48),      # row-half mode (16 rows)
+    (wl.F32, 2, 2, 16, 1, [1000, 3], 16),      # row-half, one-half-tile splits: every split's second half is empty
+    (wl.F32, 2, 1, 8, 9, [1000], 16),          # 72 rows in 16-row splits: every tile a half tile (63 splits)
     (wl.BF16, 2, 2, 16, 64, [600, 300], 112),  # bf16 matrix kernel
     (wl.FP8, 2, 2, 16, 64, [600, 300], 112),   # FP8 cache on the fp32 matrix kernel (whole tiles)
 ])
