@@ -14,7 +14,8 @@
 //    accepted node's prediction;
 //  * compaction: cache row prefix + path[j] moves to prefix + j, j = 1..k.
 //
-// Three launches on the caller's stream:
+// Launches on the caller's stream (two when the caches are given: the walk and the
+// compaction then run as one, accept_walk_compact_kernel below):
 //  * accept_argmax_kernel: one 256-thread workgroup per (batch row, node); each
 //    thread keeps the first maximum of its strided share of the V logits
 //    (coalesced, 16-byte loads four at a time when V is a multiple of 4), then a
@@ -171,6 +172,83 @@ __global__ __launch_bounds__(256) void accept_compact_kernel(char* ckv, char* k_
     }
 }
 
+// The walk and the compaction in one launch (when the caches are given): every
+// workgroup of batch row b repeats the walk on its first wave -- a few ballots
+// over at most 256 nodes -- into LDS, the one with window 0 writes the walk's
+// outputs, and each then moves its window of the accepted rows as
+// accept_compact_kernel does.  One launch fewer per step than walk + compact.
+__global__ __launch_bounds__(256) void accept_walk_compact_kernel(
+    const int32_t* __restrict__ parent, const int32_t* __restrict__ token, const int32_t* __restrict__ pred, int Q,
+    int32_t* __restrict__ path, int32_t* __restrict__ out_tokens, int32_t* __restrict__ accept_len, char* ckv,
+    char* k_rope, int lat_chunks, int rope_chunks, const ddtv_row* __restrict__ rows) {
+    __shared__ int32_t sp[kMaxQ], st[kMaxQ], sq[kMaxQ], spath[kMaxQ];
+    __shared__ int32_t sk;
+    __shared__ uint4 buf[kMaxQ - 1][kWindowChunks];   // 255 rows x 256 B
+    const int b = blockIdx.y;
+    const int w = blockIdx.x;
+    const int t = threadIdx.x;
+    const int64_t base = (int64_t)b * Q;
+    for (int i = t; i < Q; i += 256) {
+        sp[i] = parent[base + i];
+        st[i] = token[base + i];
+        sq[i] = pred[base + i];
+    }
+    __syncthreads();
+    if (t < 64) {   // the walk, on the first wave (as accept_walk_kernel)
+        const int lane = t;
+        int cur = 0, k = 0;
+        for (;;) {
+            const int want = sq[cur];
+            int next = -1;
+            for (int c0 = cur + 1; c0 < Q && next < 0; c0 += 64) {   // children have larger indices
+                const int c = c0 + lane;
+                const uint64_t hit = __ballot(c < Q && sp[c] == cur && st[c] == want);
+                if (hit) next = c0 + __ffsll((unsigned long long)hit) - 1;
+            }
+            if (next < 0) break;
+            ++k;
+            if (lane == 0) spath[k] = next;
+            cur = next;
+        }
+        if (lane == 0) {
+            spath[0] = 0;
+            sk = k;
+            if (w == 0) {
+                out_tokens[base + k] = sq[cur];
+                accept_len[b] = k;
+            }
+        }
+    }
+    __syncthreads();
+    const int k = sk;
+    if (w == 0) {
+        for (int i = t; i < Q; i += 256) {
+            path[base + i] = i <= k ? spath[i] : -1;
+            if (i < k) out_tokens[base + i] = st[spath[i + 1]];
+            else if (i > k) out_tokens[base + i] = -1;
+        }
+    }
+    if (k <= 0) return;
+    const int c_lo = w * kWindowChunks;
+    const bool lat = c_lo < lat_chunks;
+    char* cbase = lat ? ckv : k_rope;
+    const int row_chunks = lat ? lat_chunks : rope_chunks;
+    const int c0 = lat ? c_lo : c_lo - lat_chunks;
+    const int nc = min(kWindowChunks, row_chunks - c0);
+    const ddtv_row rd = rows[b];
+    const int64_t first = rd.kv_off + rd.prefix;   // cache row of tree node 0
+    uint4* arr = reinterpret_cast<uint4*>(cbase);
+    for (int e = t; e < k * kWindowChunks; e += 256) {
+        const int j = e / kWindowChunks, c = e % kWindowChunks;
+        if (c < nc) buf[j][c] = arr[(first + spath[j + 1]) * row_chunks + c0 + c];
+    }
+    __syncthreads();
+    for (int e = t; e < k * kWindowChunks; e += 256) {
+        const int j = e / kWindowChunks, c = e % kWindowChunks;
+        if (c < nc) arr[(first + j + 1) * row_chunks + c0 + c] = buf[j][c];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_tree_accept(const AcceptArgs& a, hipStream_t stream) {
@@ -179,13 +257,19 @@ hipError_t launch_tree_accept(const AcceptArgs& a, hipStream_t stream) {
                        a.logits, a.V, a.pred);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const int lat_chunks = kDLat * a.kv_elem / 16, rope_chunks = kDRope * a.kv_elem / 16;
+    const int windows = (lat_chunks + kWindowChunks - 1) / kWindowChunks +
+                        (rope_chunks + kWindowChunks - 1) / kWindowChunks;
+    if (a.ckv) {
+        hipLaunchKernelGGL(accept_walk_compact_kernel, dim3((unsigned)windows, (unsigned)a.B), dim3(256), 0, stream,
+                           a.parent, a.token, a.pred, a.Q, a.path, a.out_tokens, a.accept_len,
+                           static_cast<char*>(a.ckv), static_cast<char*>(a.k_rope), lat_chunks, rope_chunks, a.rows);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(accept_walk_kernel, dim3((unsigned)a.B), dim3(64), 0, stream, a.parent, a.token, a.pred, a.Q,
                        a.path, a.out_tokens, a.accept_len);
     e = hipGetLastError();
     if (e != hipSuccess || !a.ckv) return e;
-    const int lat_chunks = kDLat * a.kv_elem / 16, rope_chunks = kDRope * a.kv_elem / 16;
-    const int windows = (lat_chunks + kWindowChunks - 1) / kWindowChunks +
-                        (rope_chunks + kWindowChunks - 1) / kWindowChunks;
     hipLaunchKernelGGL(accept_compact_kernel, dim3((unsigned)windows, (unsigned)a.B), dim3(256), 0, stream,
                        static_cast<char*>(a.ckv), static_cast<char*>(a.k_rope), lat_chunks, rope_chunks, a.rows,
                        a.path, a.accept_len, a.Q);
