@@ -217,7 +217,11 @@ typedef struct {
     int32_t split_len;     /* KV positions per split; 0 = automatic; else a multiple of 16 (cache
                               tiles hold 32 rows; the fp32 matrix kernel on an fp32 cache runs a
                               split's last tile of at most 16 rows as half a tile, the other
-                              kernels mask the unused rows of a whole one) */
+                              kernels mask the unused rows of a whole one).  In row-half mode (the
+                              fp32 matrix kernel on batch rows of at most 32 query rows) a
+                              row's last split also takes a remainder of up to 16 positions
+                              rather than a split of its own: a row of n positions has
+                              max(1, (n + L - 1 - 16) / L) splits there, ceil(n / L) elsewhere */
     hipEvent_t attn_begin; /* if non-NULL: recorded on `stream` right before the main kernel */
     hipEvent_t attn_end;   /* if non-NULL: recorded on `stream` right after it (before the merge) */
     int32_t wg_order;      /* ddtv_wg_order */

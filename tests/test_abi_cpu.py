@@ -457,7 +457,7 @@ def workload_vis(name, q_len=None):
 @pytest.mark.parametrize("name,q_len,dtype,want", [
     ("c3", None, 0, (2, 272, 16, 256, dd.DDTV_ORDER_XCD_LOCAL)),
     ("c4", None, 0, (2, 32896, 1, 256, dd.DDTV_ORDER_XCD_LOCAL)),
-    ("c4", 1, 0, (2, 1056, 32, 256, dd.DDTV_ORDER_XCD_LOCAL)),
+    ("c4", 1, 0, (2, 1024, 32, 256, dd.DDTV_ORDER_XCD_LOCAL)),
     ("c5", None, 1, (2, None, 1, 2048, dd.DDTV_ORDER_SPREAD)),
 ])
 def test_plans_of_the_benchmarked_workloads(lib, name, q_len, dtype, want):
@@ -511,6 +511,18 @@ def test_split_lengths_off_the_tile_grid(lib):
     assert rc == 0 and (L, ns) == (32928, 1), (L, ns)
     small = fake_vis(B=1, Q=64, prefix=(1000,))           # 3.5 tiles beat 4 by more than that
     assert dd.ddtv_plan_info(small, 16, 0)[2:4] == (112, 10)
+    # in row-half mode a row's last split takes a remainder of up to 16 positions: decode rows one
+    # position past 32 x 1024 keep 32 splits of 1024, 17 past need a 33rd; the vector path, the
+    # usual matrix mode and the bf16 matrix kernel end every split at the split length
+    for extra, want in ((1, 32), (16, 32), (17, 33)):
+        dec = fake_vis(B=8, Q=1, prefix=(32767 + extra,) * 8)
+        assert dd.ddtv_plan_info(dec, 16, 0, dd.make_opts(split_len=1024))[2:4] == (1024, want), extra
+    dec = fake_vis(B=8, Q=1, prefix=(32768,) * 8)
+    assert dd.ddtv_plan_info(dec, 16, 0)[2:4] == (1024, 32)
+    assert dd.ddtv_plan_info(dec, 16, 0, dd.make_opts(split_len=1024, path=dd.DDTV_PATH_VALU))[2:4] == (1024, 33)
+    bfv = fake_vis(B=2, Q=64, prefix=(2048 + 8 - 64,) * 2)   # 2 x 1024 + 8 positions per row
+    assert dd.ddtv_plan_info(bfv, 16, dd.DDTV_BF16, dd.make_opts(split_len=1024))[2:4] == (1024, 3)
+    assert dd.ddtv_plan_info(bfv, 16, 0, dd.make_opts(split_len=1024))[2:4] == (1024, 3)
     # the other kernels keep 32-row split lengths: bf16 matrix kernel, FP8 cache, vector path
     for dtype, opts in [(dd.DDTV_BF16, None), (dd.DDTV_FP8_E4M3, None), (0, dd.make_opts(path=dd.DDTV_PATH_VALU))]:
         rc, path, L, ns, wg, order = dd.ddtv_plan_info(vis, 16, dtype, opts)

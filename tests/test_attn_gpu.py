@@ -146,6 +146,24 @@ def test_half_tile_splits(kv_dtype, path, B, H, Q, prefix, split_len):
     assert r.plan()[2] == split_len
 
 
+# Row-half mode lets a row's last split take a remainder of up to 16 positions
+# instead of starting a split for it (rows one position past a split boundary,
+# e.g. decode with q_len 1 over a 2^k prefix); the other modes do not.
+@pytest.mark.parametrize("kv_dtype,path,B,H,Q,prefix,split_len,n_split", [
+    (wl.F32, 2, 2, 16, 1, [3072, 2047], 1024, 3),   # row-half: 3073 = 3 x 1024 + 1 and 2048 = 2 x 1024
+    (wl.F32, 2, 2, 16, 4, [524, 100], 128, 5),      # usual mode: 528 = 4 x 128 + 16 keeps a fifth split
+    (wl.F32, 2, 1, 16, 64, [490], 272, 3),          # half-tile lengths: 554 = 2 x 272 + 10 keeps a third
+    (wl.BF16, 3, 2, 16, 1, [1024, 700], 512, 2),    # widened bf16, row-half: 1025 = 2 x 512 + 1
+    (wl.F32, 1, 2, 16, 1, [3072, 2047], 1024, 4),   # vector path: no remainder, 4 splits
+])
+def test_last_split_takes_the_remainder(kv_dtype, path, B, H, Q, prefix, split_len, n_split):
+    w = wl.make_workload(f"absorb{B}x{H}x{Q}", 8300 + B * 100 + H * 10 + Q, B=B, H=H, Q=Q, prefix=prefix,
+                         tree="uniform", kv_dtype=kv_dtype)
+    r, _, _ = check_full(w, path=path, split_len=split_len,
+                         what=f"last split remainder B{B} H{H} Q{Q} P{prefix} dtype {kv_dtype} split {split_len}")
+    assert r.plan()[2:4] == (split_len, n_split), r.plan()
+
+
 # Many partials on few rows: the merge shares a row's partials among 2, 4 or 8
 # thread groups and combines their results in LDS (test_split_count_invariance
 # covers 1 and 2 groups on c3).

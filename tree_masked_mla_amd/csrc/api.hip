@@ -99,6 +99,7 @@ struct Plan {
     int rows_per_wg = 0;
     int n_rt = 0;
     int split_len = 0;
+    int absorb = 0;          // see splits_of
     int n_split = 1;
     int order = DDTV_ORDER_XCD_LOCAL;
     int64_t grid = 0;
@@ -167,15 +168,15 @@ double tiles_of(int len, bool half) {
 // Total work of the grid spread evenly over all CUs, plus the merge pass: a
 // lower bound on the makespan, and one that grows with the split count (each
 // split adds its set-up and merge traffic).
-double fluid_bound(const std::vector<int>& kv, int n_rt, int L, int cus, double setup_tiles,
+double fluid_bound(const std::vector<int>& kv, int n_rt, int L, int absorb, int cus, double setup_tiles,
                    double merge_tiles_per_partial_row_split, int64_t R, bool half) {
     int n_split = 1;
-    for (int k : kv) n_split = std::max(n_split, (k + L - 1) / L);
+    for (int k : kv) n_split = std::max(n_split, splits_of(k, L, absorb));
     half = half && L % kTile != 0;   // (the kernel's half-tile variant runs only then)
     const double full_tiles = tiles_of(L, half);
     double work = 0.0, merge = 0.0;
     for (int k : kv) {
-        const int nb = (k + L - 1) / L;
+        const int nb = splits_of(k, L, absorb);
         const int last = k - (nb - 1) * L;
         work += (double)n_rt * ((double)(nb - 1) * (setup_tiles + full_tiles) + setup_tiles +
                                 tiles_of(last, half) + (double)(n_split - nb) * kExitCost);
@@ -194,25 +195,26 @@ double fluid_bound(const std::vector<int>& kv, int n_rt, int L, int cus, double 
 // query tiles of one (row, split) cost the same, so each XCD's list is
 // simulated run by run.  `bound`: give up (returning at least bound) once the
 // total work alone shows the plan cannot beat it.
-double estimate(const std::vector<int>& kv, int n_rt, int L, int cus, double setup_tiles,
+double estimate(const std::vector<int>& kv, int n_rt, int L, int absorb, int cus, double setup_tiles,
                 double merge_tiles_per_partial_row_split, int64_t R, bool half, bool spread,
                 double bound = 1e300) {
     const int per_xcd = std::max(1, std::min(kMaxCusPerXcd, cus / kXcds));
     int n_split = 1;
-    for (int k : kv) n_split = std::max(n_split, (k + L - 1) / L);
+    for (int k : kv) n_split = std::max(n_split, splits_of(k, L, absorb));
     const int64_t G = (int64_t)kv.size() * n_split * n_rt;
     half = half && L % kTile != 0;   // (the kernel's half-tile variant runs only then)
     double merge = 0.0;   // each partial row is written, then read by the merge pass
     for (int k : kv) {
-        const int parts = (k + L - 1) / L;
+        const int parts = splits_of(k, L, absorb);
         if (parts > 1) merge += merge_tiles_per_partial_row_split * (double)parts * (double)R;
     }
     auto cost = [&](int b, int s) {
-        const int len = std::min(L, kv[b] - s * L);
+        const int nb = splits_of(kv[b], L, absorb);
+        const int len = s < nb - 1 ? L : s == nb - 1 ? kv[b] - s * L : 0;
         return len > 0 ? setup_tiles + tiles_of(len, half) : kExitCost;
     };
     const double fluid =
-        fluid_bound(kv, n_rt, L, cus, setup_tiles, merge_tiles_per_partial_row_split, R, half);
+        fluid_bound(kv, n_rt, L, absorb, cus, setup_tiles, merge_tiles_per_partial_row_split, R, half);
     if (fluid >= bound) return fluid;
     if (G <= (int64_t)per_xcd * kXcds) {   // no XCD gets more items than CUs: all start at once
         int longest = 0;
@@ -398,6 +400,12 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
     // of 16), so split lengths 16 rows off the tile grid are candidates too; the
     // other kernels pay a whole tile for such a tile.
     const bool half = mfma && !p->bf16_mma && !p->halves && kv_dtype == DDTV_F32;
+    // Row-half mode lets a row's last split take a remainder of up to 16 positions
+    // (splits_of): decode rows one position past a split boundary then need no
+    // workgroup for that position.  The other kernels end every split at split_len.
+    p->absorb = p->halves ? kSplitQuantum : 0;
+    const int absorb = p->absorb;
+    const int cover = std::max(1, max_kv - absorb);   // what S equal pieces must cover
     const double setup = mfma ? 2.0 : 1.0;
     const double tile_us = p->bf16_mma ? 0.9 : (mfma ? 7.3 : 1.0);
     const double merge_per_row_split = ((half ? 2048.0 : 4096.0) / 4.0e12) * 1e6 / tile_us;   // ~4 TB/s effective
@@ -410,11 +418,11 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
         if (order_req != DDTV_ORDER_AUTO) {
             *order = order_req;
             return order_req == DDTV_ORDER_SPREAD
-                       ? estimate(kv_sorted, p->n_rt, L, cus, setup, merge_per_row_split, R, half, true, bound)
-                       : estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, half, false, bound);
+                       ? estimate(kv_sorted, p->n_rt, L, absorb, cus, setup, merge_per_row_split, R, half, true, bound)
+                       : estimate(kv, p->n_rt, L, absorb, cus, setup, merge_per_row_split, R, half, false, bound);
         }
-        const double local = estimate(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, half, false, bound);
-        const double spread = estimate(kv_sorted, p->n_rt, L, cus, setup, merge_per_row_split, R, half, true,
+        const double local = estimate(kv, p->n_rt, L, absorb, cus, setup, merge_per_row_split, R, half, false, bound);
+        const double spread = estimate(kv_sorted, p->n_rt, L, absorb, cus, setup, merge_per_row_split, R, half, true,
                                        std::min(bound, local * 0.98));
         *order = spread < local * 0.98 ? DDTV_ORDER_SPREAD : DDTV_ORDER_XCD_LOCAL;
         return std::min(local, spread);
@@ -437,12 +445,12 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
         int prevLh = 0;
         auto try_half = [&](int S, int L) {
             if (!half) return;
-            const int Lh = (int)round_up((size_t)((max_kv + S - 1) / S), kSplitQuantum);
+            const int Lh = (int)round_up((size_t)((cover + S - 1) / S), kSplitQuantum);
             if (Lh == L || Lh == prevLh) return;
             prevLh = Lh;
             int64_t wh = 0;
-            for (int b = 0; b < vis->B; ++b) wh += (int64_t)((kv[b] + Lh - 1) / Lh) * p->n_rt;
-            if (wh > cus || (S > 1 && partial_bytes(vis->B, R, (max_kv + Lh - 1) / Lh) > ws_cap)) return;
+            for (int b = 0; b < vis->B; ++b) wh += (int64_t)splits_of(kv[b], Lh, absorb) * p->n_rt;
+            if (wh > cus || (S > 1 && partial_bytes(vis->B, R, splits_of(max_kv, Lh, absorb)) > ws_cap)) return;
             int order = DDTV_ORDER_XCD_LOCAL;
             const double e = cost_at(Lh, &order, best * 0.98);
             if (e < best * 0.98) {
@@ -454,7 +462,7 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
         int prevL = 0, worse = 0;
         // (every S below 32, then steps of S / 32: the split lengths grow dense)
         for (int S = 1;; S += S < 32 ? 1 : S / 32) {
-            const int L = (int)round_up((size_t)((max_kv + S - 1) / S), kTile);
+            const int L = (int)round_up((size_t)((cover + S - 1) / S), kTile);
             if (L < 4 * kTile && S > 1) break;
             if (L == prevL) {
                 try_half(S, L);
@@ -462,11 +470,11 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
             }
             prevL = L;
             int64_t wgs = 0;
-            for (int b = 0; b < vis->B; ++b) wgs += (int64_t)((kv[b] + L - 1) / L) * p->n_rt;
+            for (int b = 0; b < vis->B; ++b) wgs += (int64_t)splits_of(kv[b], L, absorb) * p->n_rt;
             if (wgs > wg_cap && S > 1) break;
-            const int parts_L = (max_kv + L - 1) / L;
+            const int parts_L = splits_of(max_kv, L, absorb);
             if (S > 1 && partial_bytes(vis->B, R, parts_L) > ws_cap) break;   // more splits only need more
-            if (S > 1 && fluid_bound(kv, p->n_rt, L, cus, setup, merge_per_row_split, R, half) >= best * 0.98)
+            if (S > 1 && fluid_bound(kv, p->n_rt, L, absorb, cus, setup, merge_per_row_split, R, half) >= best * 0.98)
                 break;   // its lower bound cannot beat the best by 2 %, nor can more splits'
             int order = DDTV_ORDER_XCD_LOCAL;
             const double e = cost_at(L, &order, best * 0.98);   // a plan must beat the best by 2 %
@@ -484,7 +492,7 @@ ddtv_status make_plan_uncached(const ddtv_vis* vis, int32_t H, ddtv_dtype kv_dty
         p->split_len = bestL;
         p->order = bestOrder;
     }
-    p->n_split = (max_kv + p->split_len - 1) / p->split_len;
+    p->n_split = std::max(1, splits_of(max_kv, p->split_len, p->absorb));
     p->grid = (int64_t)vis->B * p->n_rt * p->n_split;
     if (!grid_fits(p->grid, 512)) return DDTV_EUNSUPPORTED;   // 512 = the largest attention workgroup
     const int parts = p->n_split;   // partials per batch row
@@ -561,6 +569,7 @@ ddtv_status launch_verify(const Plan& p, const float* q_abs, const float* q_rope
     a.R = vis->Q * H;
     a.n_rt = p.n_rt;
     a.split_len = p.split_len;
+    a.absorb = p.absorb;
     a.n_split = p.n_split;
     a.spread = p.order == DDTV_ORDER_SPREAD;
     a.halves = p.halves;

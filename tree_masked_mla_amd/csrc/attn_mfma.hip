@@ -438,9 +438,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, Smem& sm, int b, in
 
     const ddtv_row rowd = a.rows[b];
     const int kv_len = rowd.kv_len, P = rowd.prefix;
-    const int n_b = (kv_len + a.split_len - 1) / a.split_len;
+    // (row-half mode: the last split takes the remainder a.absorb allows; the usual
+    // mode's plans set no remainder)
+    const int n_b = kHv ? splits_of(kv_len, a.split_len, a.absorb) : (kv_len + a.split_len - 1) / a.split_len;
     const int kv_lo = s * a.split_len;
-    const int kv_hi = min(kv_len, kv_lo + a.split_len);
+    const int kv_hi = kHv ? (s == n_b - 1 ? kv_len : kv_lo + a.split_len) : min(kv_len, kv_lo + a.split_len);
     const int ntiles = (kv_hi - kv_lo + kTile - 1) / kTile;
     const int64_t kv_base = rowd.kv_off;
 
@@ -616,7 +618,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(AttnArgs a) {
     const int s = (int)((w / a.n_rt) % a.n_split);
     const int b = batch_row(a, (int)(w / ((int64_t)a.n_rt * a.n_split)));
     const int kv_len = a.rows[b].kv_len;
-    if (s * a.split_len >= kv_len) return;   // this batch row needs fewer splits
+    if (kHv ? s >= splits_of(kv_len, a.split_len, a.absorb) : s * a.split_len >= kv_len)
+        return;   // this batch row needs fewer splits
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (wave & 1)

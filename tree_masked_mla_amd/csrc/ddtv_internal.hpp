@@ -39,6 +39,8 @@ struct AttnArgs {
     int spread;              // 1: work item = workgroup id; 0: XCD-local order (xcd_remap)
     int halves;              // 1: row-half mode (32 rows per workgroup, halves combined in it; matrix kernel)
     float scale_log2;        // scale * log2(e)
+    int absorb;              // a row's last split also takes a remainder of up to this many positions
+                             // (row-half mode; 0 for the other kernels, whose splits stop at split_len)
 };
 
 // Everything the draft-tree builder needs (passed by value).
@@ -90,6 +92,16 @@ hipError_t launch_tree_build(const TreeArgs& a, hipStream_t stream);
 hipError_t launch_tree_accept(const AcceptArgs& a, hipStream_t stream);
 
 constexpr int kValuRows = 16;   // query rows per VALU workgroup
+
+// Splits of a batch row of kv_len positions at split length L: split s starts at
+// s * L and ends L later, except the last, which ends at kv_len; it also takes a
+// remainder of up to `absorb` positions rather than leaving them to a split of
+// their own (a row one position past a multiple of L would otherwise hold up a
+// whole extra workgroup of the grid for that position).
+__host__ __device__ __forceinline__ int splits_of(int kv_len, int L, int absorb) {
+    const int n = (kv_len + L - 1 - absorb) / L;
+    return kv_len <= 0 ? 0 : (n < 1 ? 1 : n);
+}
 
 // Work item of workgroup i in the XCD-local order: consecutive work items land
 // on the same XCD (the dispatcher deals workgroup i to XCD i % 8).  Bijective for

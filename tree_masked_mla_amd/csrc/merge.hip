@@ -36,7 +36,7 @@ __global__ __launch_bounds__(G == 1 ? 256 : 128 * G) void merge_kernel(AttnArgs 
     const int b = (int)(gr / a.R);
     const int row = (int)(gr - (int64_t)b * a.R);
     const int kv_len = a.rows[b].kv_len;
-    const int n_b = (kv_len + a.split_len - 1) / a.split_len;   // this batch row's partials
+    const int n_b = splits_of(kv_len, a.split_len, a.absorb);   // this batch row's partials
     if (n_b <= 1) return;
     const int c = threadIdx.x & 127;
     const int64_t pbase = (int64_t)b * a.n_split * a.R + row;   // partial s at pbase + s * R
